@@ -1,0 +1,258 @@
+/*
+ * attn_ref.c -- plain fp64 CPU oracle for batched attention over a paged KV
+ * cache viewed as a block-sparse-row matrix.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library calls, links or
+ * includes this file; only the tests, the smoke check and the CPU-baseline leg
+ * of the benchmark load it.  It shares no code, header or helper with the GPU
+ * path.
+ *
+ * What it computes (FlashInfer MLSys 2025 pages):
+ *   - page table walk: request i's logical token j lives in physical page
+ *     kv_indices[kv_indptr[i] + j / P] at slot j % P ("Page-Level Attention",
+ *     the request 0 / request 1 page-table example on the serving-engine page);
+ *     the last page holds kv_last_page_len[i] valid tokens (index arrays named
+ *     in "The Interface" code block);
+ *   - exact attention softmax(s) V over the visible keys, with s = scale * q.k,
+ *     an optional logits soft-cap transform s <- cap * tanh(s / cap) (the
+ *     "logits transform such as soft-capping" of the JIT paragraph), GQA head
+ *     grouping (query head h reads KV head h / G, "Head Group Packing"), and the
+ *     causal mask of batch prefill (causal=True in "The Interface");
+ *   - the (output, log-sum-exp) state of each query row, the quantity that
+ *     FlashDecoding partials and merge_state combine ("FlashDecoding: Parallel
+ *     KV Split"; "merge partial results with the log-sum-exp composition" in
+ *     the load-balancing paragraph).
+ *
+ * Method: naive per-token page gather and a plain two-pass softmax (max, then
+ * exp-sum), all in double precision.  No tiling, no online rescaling.
+ *
+ * Readings where the pages are silent (each listed in the design notes):
+ *   - KV head of query head h is h / G with G = Hq / Hk (contiguous groups);
+ *   - causal alignment is bottom-right: query token t of a request with
+ *     qo_len queries and kv_len keys sees keys j <= kv_len - qo_len + t;
+ *   - the soft-cap applies to the already-scaled logit;
+ *   - a row with no visible key has o = 0 and lse = -inf;
+ *   - lse is the natural-log log-sum-exp of the (capped) logits.
+ *
+ * Parity pins: see the oracle tests (dense brute force, library SDPA, closed
+ * forms, the pages' page-table example, page-permutation invariance,
+ * split+merge == unsplit, cascade == flat).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OREF_OK 0
+#define OREF_EINVAL -1
+#define OREF_ENOMEM -2
+
+static char g_err[256];
+
+const char *oref_last_error(void) { return g_err; }
+
+static int fail(const char *msg, long long a, long long b) {
+  snprintf(g_err, sizeof(g_err), "%s (%lld, %lld)", msg, a, b);
+  return OREF_EINVAL;
+}
+
+/* Number of valid keys of request i: (pages - 1) * P + last_page_len, or 0. */
+static int64_t kv_len_of(const int32_t *kv_indptr, const int32_t *last, int i, int P) {
+  int64_t np = (int64_t)kv_indptr[i + 1] - kv_indptr[i];
+  if (np == 0) return 0;
+  return (np - 1) * P + last[i];
+}
+
+static int64_t qo_len_of(const int32_t *qo_indptr, int i) {
+  return qo_indptr ? (int64_t)qo_indptr[i + 1] - qo_indptr[i] : 1;
+}
+
+static int64_t qo_start_of(const int32_t *qo_indptr, int i) {
+  return qo_indptr ? (int64_t)qo_indptr[i] : (int64_t)i;
+}
+
+/*
+ * Validate the index arrays (written separately from the library's own checks).
+ * Rules: B >= 0; indptr[0] == 0 and non-decreasing; 1 <= last <= P for a
+ * request with pages; page ids in [0, pool_pages); Hq % Hk == 0; causal needs
+ * qo_len <= kv_len for a request with two or more queries (a single-query
+ * request may have an empty cache: its row then sees no key).
+ */
+int oref_validate(int B, const int32_t *qo_indptr, const int32_t *kv_indptr,
+                  const int32_t *kv_indices, const int32_t *kv_last_page_len, int P,
+                  int Hq, int Hk, int D, int causal, int64_t pool_pages) {
+  if (B < 0) return fail("negative batch", B, 0);
+  if (P < 1) return fail("page_size < 1", P, 0);
+  if (Hq < 1 || Hk < 1 || Hq % Hk != 0) return fail("bad head counts", Hq, Hk);
+  if (D < 1) return fail("bad head_dim", D, 0);
+  if (kv_indptr[0] != 0) return fail("kv_indptr[0] != 0", kv_indptr[0], 0);
+  if (qo_indptr && qo_indptr[0] != 0) return fail("qo_indptr[0] != 0", qo_indptr[0], 0);
+  for (int i = 0; i < B; ++i) {
+    if (kv_indptr[i + 1] < kv_indptr[i]) return fail("kv_indptr decreases", i, kv_indptr[i + 1]);
+    if (qo_indptr && qo_indptr[i + 1] < qo_indptr[i]) return fail("qo_indptr decreases", i, qo_indptr[i + 1]);
+    int64_t np = (int64_t)kv_indptr[i + 1] - kv_indptr[i];
+    if (np > 0 && (kv_last_page_len[i] < 1 || kv_last_page_len[i] > P))
+      return fail("last_page_len out of [1, P]", i, kv_last_page_len[i]);
+    for (int64_t p = kv_indptr[i]; p < kv_indptr[i + 1]; ++p)
+      if (kv_indices[p] < 0 || kv_indices[p] >= pool_pages) return fail("page id out of pool", i, kv_indices[p]);
+    if (causal && qo_len_of(qo_indptr, i) >= 2 &&
+        qo_len_of(qo_indptr, i) > kv_len_of(kv_indptr, kv_last_page_len, i, P))
+      return fail("causal with qo_len > kv_len", i, qo_len_of(qo_indptr, i));
+  }
+  return OREF_OK;
+}
+
+/* Physical location of logical token j of request i: page id and slot. */
+int oref_token_location(const int32_t *kv_indptr, const int32_t *kv_indices, int P, int i,
+                        int64_t j, int32_t *page, int32_t *slot) {
+  int64_t np = (int64_t)kv_indptr[i + 1] - kv_indptr[i];
+  if (j < 0 || j / P >= np) return fail("token beyond the request's pages", i, j);
+  *page = kv_indices[kv_indptr[i] + j / P];
+  *slot = (int32_t)(j % P);
+  return OREF_OK;
+}
+
+/* Element (page, kv, slot, head, d) of the pool [pages, 2, P, Hk, D]. */
+static inline double pool_at(const double *pool, int64_t page, int kv, int64_t slot, int g,
+                             int d, int P, int Hk, int D) {
+  return pool[((((page * 2 + kv) * P + slot) * Hk) + g) * (int64_t)D + d];
+}
+
+/*
+ * Attention for an explicit list of query rows (request, token-in-request,
+ * query head).  o is [n_rows, D], lse is [n_rows].  q is [total_qo, Hq, D].
+ */
+int oref_attention_rows(int B, const int32_t *qo_indptr, const int32_t *kv_indptr,
+                        const int32_t *kv_indices, const int32_t *kv_last_page_len, int P,
+                        int Hq, int Hk, int D, int causal, double sm_scale, double soft_cap,
+                        const double *q, const double *pool, int64_t pool_pages,
+                        int64_t n_rows, const int32_t *row_req, const int32_t *row_tok,
+                        const int32_t *row_head, double *o, double *lse) {
+  int rc = oref_validate(B, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, P, Hq, Hk, D,
+                         causal, pool_pages);
+  if (rc) return rc;
+  for (int64_t r = 0; r < n_rows; ++r) {
+    int i = row_req[r];
+    if (i < 0 || i >= B) return fail("row request out of range", r, i);
+    if (row_tok[r] < 0 || row_tok[r] >= qo_len_of(qo_indptr, i)) return fail("row token out of range", r, row_tok[r]);
+    if (row_head[r] < 0 || row_head[r] >= Hq) return fail("row head out of range", r, row_head[r]);
+  }
+  const int G = Hq / Hk;
+  int rc_all = OREF_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const int i = row_req[r];
+    const int t = row_tok[r];
+    const int h = row_head[r];
+    const int g = h / G;
+    const int64_t kv_len = kv_len_of(kv_indptr, kv_last_page_len, i, P);
+    const int64_t qo_len = qo_len_of(qo_indptr, i);
+    const int64_t limit = causal ? kv_len - qo_len + t + 1 : kv_len;
+    const double *qrow = q + ((qo_start_of(qo_indptr, i) + t) * (int64_t)Hq + h) * D;
+    double *orow = o + r * (int64_t)D;
+    if (limit <= 0) {
+      for (int d = 0; d < D; ++d) orow[d] = 0.0;
+      lse[r] = -INFINITY;
+      continue;
+    }
+    double *s = (double *)malloc(sizeof(double) * (size_t)limit);
+    if (!s) {
+#pragma omp critical
+      rc_all = OREF_ENOMEM;
+      continue;
+    }
+    /* pass 1: logits of every visible key, gathered one token at a time */
+    double m = -INFINITY;
+    for (int64_t j = 0; j < limit; ++j) {
+      int64_t page = kv_indices[kv_indptr[i] + j / P];
+      int64_t slot = j % P;
+      double acc = 0.0;
+      for (int d = 0; d < D; ++d) acc += qrow[d] * pool_at(pool, page, 0, slot, g, d, P, Hk, D);
+      acc *= sm_scale;
+      if (soft_cap > 0.0) acc = soft_cap * tanh(acc / soft_cap);
+      s[j] = acc;
+      if (acc > m) m = acc;
+    }
+    /* pass 2: normaliser and weighted sum of values */
+    double z = 0.0;
+    for (int d = 0; d < D; ++d) orow[d] = 0.0;
+    for (int64_t j = 0; j < limit; ++j) {
+      int64_t page = kv_indices[kv_indptr[i] + j / P];
+      int64_t slot = j % P;
+      double w = exp(s[j] - m);
+      z += w;
+      for (int d = 0; d < D; ++d) orow[d] += w * pool_at(pool, page, 1, slot, g, d, P, Hk, D);
+    }
+    for (int d = 0; d < D; ++d) orow[d] /= z;
+    lse[r] = m + log(z);
+    free(s);
+  }
+  return rc_all;
+}
+
+/*
+ * Every query row of the batch: o is [total_qo, Hq, D], lse is [total_qo, Hq].
+ */
+int oref_attention(int B, const int32_t *qo_indptr, const int32_t *kv_indptr,
+                   const int32_t *kv_indices, const int32_t *kv_last_page_len, int P, int Hq,
+                   int Hk, int D, int causal, double sm_scale, double soft_cap, const double *q,
+                   const double *pool, int64_t pool_pages, double *o, double *lse) {
+  int64_t total = 0;
+  for (int i = 0; i < B; ++i) total += qo_len_of(qo_indptr, i);
+  int64_t n = total * Hq;
+  int32_t *rq = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n ? n : 1));
+  int32_t *rt = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n ? n : 1));
+  int32_t *rh = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n ? n : 1));
+  if (!rq || !rt || !rh) {
+    free(rq); free(rt); free(rh);
+    return OREF_ENOMEM;
+  }
+  int64_t r = 0;
+  for (int i = 0; i < B; ++i)
+    for (int64_t t = 0; t < qo_len_of(qo_indptr, i); ++t)
+      for (int h = 0; h < Hq; ++h) {
+        rq[r] = i; rt[r] = (int32_t)t; rh[r] = h; ++r;
+      }
+  int rc = oref_attention_rows(B, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, P, Hq, Hk,
+                               D, causal, sm_scale, soft_cap, q, pool, pool_pages, n, rq, rt, rh,
+                               o, lse);
+  free(rq); free(rt); free(rh);
+  return rc;
+}
+
+/*
+ * Combine k attention states of the same query rows by log-sum-exp
+ * composition ("merge_state" in the cascade code block; the FlashDecoding
+ * merge step).  o_parts is [k, n, D], lse_parts is [k, n]; results are
+ * [n, D] and [n].  With M = max lse_k:
+ *   lse = M + ln sum_k exp(lse_k - M),  o = sum_k exp(lse_k - lse) o_k.
+ * If every lse_k is -inf the result is (0, -inf).
+ */
+int oref_merge_states(int k, int64_t n, int D, const double *o_parts, const double *lse_parts,
+                      double *o_out, double *lse_out) {
+  if (k < 1 || n < 0 || D < 1) return fail("bad merge sizes", k, n);
+  for (int64_t r = 0; r < n; ++r) {
+    double M = -INFINITY;
+    for (int c = 0; c < k; ++c) {
+      double v = lse_parts[(int64_t)c * n + r];
+      if (v > M) M = v;
+    }
+    double *orow = o_out + r * (int64_t)D;
+    for (int d = 0; d < D; ++d) orow[d] = 0.0;
+    if (M == -INFINITY) {
+      lse_out[r] = -INFINITY;
+      continue;
+    }
+    double z = 0.0;
+    for (int c = 0; c < k; ++c) z += exp(lse_parts[(int64_t)c * n + r] - M);
+    double L = M + log(z);
+    for (int c = 0; c < k; ++c) {
+      double w = exp(lse_parts[(int64_t)c * n + r] - L);
+      const double *src = o_parts + ((int64_t)c * n + r) * D;
+      for (int d = 0; d < D; ++d) orow[d] += w * src[d];
+    }
+    lse_out[r] = L;
+  }
+  return OREF_OK;
+}

@@ -1,0 +1,240 @@
+"""Plan oracle: the CPU-side work partition, written step by step in pure Python.
+
+TEST INFRASTRUCTURE ONLY.
+
+The pages describe the plan only in words: each generation step, a CPU-side
+plan splits long KV sequences into equal chunks across the GPU's processors and
+records where partial results go; persistent kernels with fixed grids then run
+it and merge the partials by log-sum-exp composition (FlashInfer paper page,
+"Load balancing that survives CUDA graphs"); the scheduler inspects the lengths
+ahead of time and balances deterministically with a cost model (talk page,
+"Runtime Scheduler for Dynamic Problem Shapes"); the query tile size is picked
+from the batch's average query length (paper page, JIT paragraph).  Where they
+stop, this module takes the plainest reading (cost = KV pages; equal-size
+contiguous segments of the concatenated page stream, one per worker) and
+spells out every step:
+
+P1 validate; P2 per-request pages, kv_len, qo_len; P3 classify requests
+(qo_len 0: nothing, 1: a decode row, >= 2: prefill tiles); P4 prefill tile
+size BR; P5 rows in request order; P6 per stream, cost C = sum of visible
+pages, segment size S = max(min_seg_pages, ceil(C / W)), row r occupies stream
+positions [c_r, c_r + vis_r), worker w owns [w S, (w + 1) S); P7 one item per
+(row, worker) overlap, a row without visible pages gets one empty item; P8
+rows with k >= 2 items get k consecutive partial slots; P9 emit int32 arrays.
+
+Parity against the pages: unpinned (they print no plan); the tests pin this
+module by invariants and by an independent brute-force partition.
+"""
+from __future__ import annotations
+
+FI_OK = 0
+FI_ERR_INVALID_ARG = -1
+FI_ERR_UNSUPPORTED = -2
+
+MAGIC = 0x31504946
+VERSION = 1
+HEADER_INTS = 64
+STREAM_DESC_INTS = 20
+STREAM0_AT = 12
+STREAM1_AT = 32
+MAX_TILE_ROWS = 128
+INT32_MAX = 2 ** 31 - 1
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def _next_pow2(x: int) -> int:
+    p = 1
+    while p < x:
+        p *= 2
+    return p
+
+
+def _align64(n: int) -> int:
+    """Round a float count up to a multiple of 64 floats (256 bytes)."""
+    return _ceil_div(n, 64) * 64
+
+
+def validate(B, qo_indptr, kv_indptr, kv_last_page_len, P, Hq, Hk, D, causal, W_d, W_p,
+             min_seg_pages, br_override, no_split):
+    """P1.  Returns (code, message)."""
+    if B < 0:
+        return FI_ERR_INVALID_ARG, "negative batch size"
+    if P < 1:
+        return FI_ERR_INVALID_ARG, "page_size < 1"
+    if Hq < 1 or Hk < 1 or Hq % Hk != 0:
+        return FI_ERR_INVALID_ARG, "head counts"
+    if D not in (64, 128):
+        return FI_ERR_UNSUPPORTED, "head_dim"
+    if Hq // Hk not in (1, 2, 4, 8):
+        return FI_ERR_UNSUPPORTED, "group size"
+    if W_d < 1 or W_p < 1:
+        return FI_ERR_INVALID_ARG, "workers < 1"
+    if min_seg_pages < 1:
+        return FI_ERR_INVALID_ARG, "min_seg_pages < 1"
+    if br_override not in (0, 16, 32, 64, 128):
+        return FI_ERR_INVALID_ARG, "br_override"
+    if no_split not in (0, 1):
+        return FI_ERR_INVALID_ARG, "no_split"
+    if len(kv_indptr) != B + 1 or len(kv_last_page_len) < B:
+        return FI_ERR_INVALID_ARG, "array lengths"
+    if qo_indptr is not None and len(qo_indptr) != B + 1:
+        return FI_ERR_INVALID_ARG, "array lengths"
+    if kv_indptr[0] != 0:
+        return FI_ERR_INVALID_ARG, "kv_indptr[0]"
+    if qo_indptr is not None and qo_indptr[0] != 0:
+        return FI_ERR_INVALID_ARG, "qo_indptr[0]"
+    for i in range(B):
+        npg = int(kv_indptr[i + 1]) - int(kv_indptr[i])
+        if npg < 0:
+            return FI_ERR_INVALID_ARG, "kv_indptr decreases"
+        qo = 1 if qo_indptr is None else int(qo_indptr[i + 1]) - int(qo_indptr[i])
+        if qo < 0:
+            return FI_ERR_INVALID_ARG, "qo_indptr decreases"
+        if npg > 0 and not (1 <= int(kv_last_page_len[i]) <= P):
+            return FI_ERR_INVALID_ARG, "last_page_len"
+        kv = 0 if npg == 0 else (npg - 1) * P + int(kv_last_page_len[i])
+        if kv > INT32_MAX:
+            return FI_ERR_INVALID_ARG, "kv_len too large"
+        if causal and qo >= 2 and qo > kv:
+            return FI_ERR_INVALID_ARG, "causal with qo_len > kv_len"
+    return FI_OK, ""
+
+
+def _partition(rows_vis, W, S, no_split):
+    """P6-P8 for one stream.  rows_vis[r] = visible pages of row r.
+    Returns (items sorted by (worker, row), wip, merge_indptr, split_rows)."""
+    items = []  # (w, r, page_begin, page_end)
+    if no_split:
+        for r, vis in enumerate(rows_vis):
+            items.append((r % W, r, 0, vis))
+    else:
+        c = 0
+        for r, vis in enumerate(rows_vis):
+            if vis == 0:
+                items.append((min(c // S, W - 1), r, 0, 0))
+            else:
+                for w in range(c // S, (c + vis - 1) // S + 1):
+                    lo = max(c, w * S)
+                    hi = min(c + vis, (w + 1) * S)
+                    items.append((w, r, lo - c, hi - c))
+            c += vis
+    items.sort(key=lambda it: (it[0], it[1]))
+    # P8: rows split over k >= 2 items get k consecutive slots (row order,
+    # then page_begin order inside the row).
+    per_row = [[] for _ in rows_vis]
+    for idx, (w, r, pb, pe) in enumerate(items):
+        per_row[r].append((pb, idx))
+    slot_of_item = [-1] * len(items)
+    merge_indptr = [0]
+    split_rows = []
+    for r, lst in enumerate(per_row):
+        k = len(lst)
+        base = merge_indptr[-1]
+        if k >= 2:
+            split_rows.append(r)
+            for j, (pb, idx) in enumerate(sorted(lst)):
+                slot_of_item[idx] = base + j
+            merge_indptr.append(base + k)
+        else:
+            merge_indptr.append(base)
+    wip = [0] * (W + 1)
+    for (w, r, pb, pe) in items:
+        wip[w + 1] += 1
+    for w in range(W):
+        wip[w + 1] += wip[w]
+    out_items = [(r, pb, pe, slot_of_item[idx]) for idx, (w, r, pb, pe) in enumerate(items)]
+    return out_items, wip, merge_indptr, split_rows
+
+
+def plan(qo_indptr, kv_indptr, kv_last_page_len, *, page_size, num_qo_heads, num_kv_heads,
+         head_dim, causal, workers_decode, workers_prefill, min_seg_pages=8, br_override=0,
+         no_split=0):
+    """Build the plan.  Returns (code, result) where result is a dict with the
+    header scalars, each stream's arrays and the flat int32 buffer."""
+    B = len(kv_indptr) - 1
+    P, Hq, Hk, D = page_size, num_qo_heads, num_kv_heads, head_dim
+    qo_indptr = None if qo_indptr is None else [int(x) for x in qo_indptr]
+    kv_indptr = [int(x) for x in kv_indptr]
+    last = [int(x) for x in kv_last_page_len]
+    code, msg = validate(B, qo_indptr, kv_indptr, last, P, Hq, Hk, D, int(bool(causal)),
+                         workers_decode, workers_prefill, min_seg_pages, br_override, no_split)
+    if code != FI_OK:
+        return code, msg
+    G = Hq // Hk
+    # P2
+    npages = [kv_indptr[i + 1] - kv_indptr[i] for i in range(B)]
+    kv_len = [0 if npages[i] == 0 else (npages[i] - 1) * P + last[i] for i in range(B)]
+    qo_len = [1] * B if qo_indptr is None else [qo_indptr[i + 1] - qo_indptr[i] for i in range(B)]
+    # P3
+    decode_reqs = [i for i in range(B) if qo_len[i] == 1]
+    prefill_reqs = [i for i in range(B) if qo_len[i] >= 2]
+    # P4
+    if br_override:
+        BR = br_override
+    elif prefill_reqs:
+        mean = _ceil_div(G * sum(qo_len[i] for i in prefill_reqs), len(prefill_reqs))
+        BR = min(MAX_TILE_ROWS, max(16, _next_pow2(mean)))
+    else:
+        BR = 0
+    # P5
+    rows_d = [(i, 0, G, npages[i]) for i in decode_reqs]
+    rows_p = []
+    for i in prefill_reqs:
+        n_packed = qo_len[i] * G
+        for k in range(_ceil_div(n_packed, BR)):
+            rb, re = k * BR, min((k + 1) * BR, n_packed)
+            tok_hi = (re - 1) // G
+            vis = kv_len[i] - qo_len[i] + tok_hi + 1 if causal else kv_len[i]
+            rows_p.append((i, rb, re, _ceil_div(vis, P)))
+    # float workspace regions (float units, each a multiple of 64 floats)
+    cap_d = 2 * (workers_decode - 1)
+    cap_p = 2 * (workers_prefill - 1)
+    sizes = [_align64(cap_d * Hq * D), _align64(cap_d * Hq),
+             _align64(cap_p * Hk * MAX_TILE_ROWS * D), _align64(cap_p * Hk * MAX_TILE_ROWS)]
+    ws_off = [0, sizes[0], sizes[0] + sizes[1], sizes[0] + sizes[1] + sizes[2]]
+    ws_total = sum(sizes)
+    if ws_total > INT32_MAX:
+        return FI_ERR_INVALID_ARG, "workspace too large for the workers given"
+
+    streams = []
+    for kind, rows, W, tile in ((0, rows_d, workers_decode, G), (1, rows_p, workers_prefill, BR)):
+        vis = [r[3] for r in rows]
+        C = sum(vis)
+        S = max(min_seg_pages, _ceil_div(C, W))
+        items, wip, merge_indptr, split_rows = _partition(vis, W, S, no_split)
+        streams.append(dict(kind=kind, W=W, S=S, BR=tile, rows=rows, items=items, wip=wip,
+                            merge_indptr=merge_indptr, split_rows=split_rows,
+                            n_slots=merge_indptr[-1],
+                            slot_cap=cap_d if kind == 0 else cap_p,
+                            ws_off_o=ws_off[0] if kind == 0 else ws_off[2],
+                            ws_off_lse=ws_off[1] if kind == 0 else ws_off[3]))
+    # P9: flat buffer
+    buf = [0] * HEADER_INTS
+    for st in streams:
+        st["off_rows"] = len(buf)
+        for r in st["rows"]:
+            buf.extend(r)
+        st["off_items"] = len(buf)
+        for it in st["items"]:
+            buf.extend(it)
+        st["off_wip"] = len(buf)
+        buf.extend(st["wip"])
+        st["off_merge_indptr"] = len(buf)
+        buf.extend(st["merge_indptr"])
+        st["off_split"] = len(buf)
+        buf.extend(st["split_rows"])
+    head = [MAGIC, VERSION, len(buf), B, sum(qo_len), Hq, Hk, D, P, int(bool(causal)), G,
+            ws_total]
+    buf[:len(head)] = head
+    for at, st in ((STREAM0_AT, streams[0]), (STREAM1_AT, streams[1])):
+        desc = [st["W"], st["S"], st["BR"], len(st["rows"]), len(st["items"]), st["n_slots"],
+                len(st["split_rows"]), st["slot_cap"], st["off_rows"], st["off_items"],
+                st["off_wip"], st["off_merge_indptr"], st["off_split"], st["ws_off_o"],
+                st["ws_off_lse"], st["kind"], 0, 0, 0, 0]
+        buf[at:at + STREAM_DESC_INTS] = desc
+    result = dict(B=B, total_qo=sum(qo_len), G=G, ws_floats=ws_total, decode=streams[0],
+                  prefill=streams[1], buf=buf, kv_len=kv_len, qo_len=qo_len)
+    return FI_OK, result

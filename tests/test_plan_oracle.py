@@ -1,0 +1,216 @@
+"""Pins of the plan oracle (oracle/plan_ref.py).
+
+The pages print no plan, so the oracle is pinned by what its rules imply:
+- a brute-force partition that walks the page stream one position at a time
+  and cuts it wherever the owning worker or the row changes;
+- invariants: every row's visible pages are covered exactly once and in order,
+  no worker holds more than S pages, items <= rows + W - 1, slots <= 2 (W - 1),
+  slot numbering, worker item ranges;
+- the tile-size rule on the worked values (mean query length 960 -> 128,
+  256 -> 128, 12 -> 16);
+- validation codes.
+"""
+import bisect
+
+import numpy as np
+import pytest
+
+from oracle import plan_ref as pr
+
+
+def _random_case(rng, B, max_qo, max_kv, P, causal):
+    qo = rng.integers(0, max_qo + 1, size=B)
+    kv = np.array([rng.integers(q if (causal and q >= 2) else 0, max(q, max_kv) + 1) for q in qo])
+    npg = -(-kv // P)
+    last = np.where(npg > 0, kv - (npg - 1) * P, 0).astype(np.int32)
+    kv_indptr = np.concatenate([[0], np.cumsum(npg)]).astype(np.int32)
+    qo_indptr = np.concatenate([[0], np.cumsum(qo)]).astype(np.int32)
+    return qo_indptr, kv_indptr, last, qo, kv
+
+
+def brute_force_items(vis, W, S):
+    """Walk the stream position by position; emit (w, r, pb, pe) runs."""
+    c = np.concatenate([[0], np.cumsum(vis)]).astype(np.int64)
+    out = []
+    for r, v in enumerate(vis):
+        if v == 0:
+            out.append((min(int(c[r]) // S, W - 1), r, 0, 0))
+    C = int(c[-1])
+    run = None
+    for pos in range(C):
+        r = bisect.bisect_right(c, pos) - 1
+        while vis[r] == 0:
+            r += 1
+        w = pos // S
+        if run and run[0] == w and run[1] == r:
+            run[3] += 1
+        else:
+            if run:
+                out.append(tuple(run))
+            run = [w, r, pos - int(c[r]), pos - int(c[r]) + 1]
+    if run:
+        out.append(tuple(run))
+    return sorted(out, key=lambda t: (t[0], t[1]))
+
+
+def _check_stream(st, no_split):
+    W, S = st["W"], st["S"]
+    rows, items, wip = st["rows"], st["items"], st["wip"]
+    vis = [r[3] for r in rows]
+    assert wip[0] == 0 and wip[-1] == len(items)
+    assert all(wip[w] <= wip[w + 1] for w in range(W))
+    owner = np.zeros(len(items), int)
+    for w in range(W):
+        owner[wip[w]:wip[w + 1]] = w
+        rs = [items[k][0] for k in range(wip[w], wip[w + 1])]
+        assert rs == sorted(rs)
+    per_row = {r: [] for r in range(len(rows))}
+    for k, (r, pb, pe, slot) in enumerate(items):
+        per_row[r].append((pb, pe, slot, owner[k]))
+    mi = st["merge_indptr"]
+    assert len(mi) == len(rows) + 1 and mi[0] == 0
+    for r, lst in per_row.items():
+        lst.sort()
+        assert len(lst) >= 1
+        # coverage: contiguous, exactly once, in order
+        pos = 0
+        for pb, pe, slot, w in lst:
+            assert pb == pos and pe >= pb
+            pos = pe
+        assert pos == vis[r]
+        if len(lst) == 1:
+            assert lst[0][2] == -1 and mi[r + 1] == mi[r]
+        else:
+            assert [x[2] for x in lst] == list(range(mi[r], mi[r] + len(lst)))
+            assert mi[r + 1] - mi[r] == len(lst)
+    assert st["split_rows"] == [r for r, lst in per_row.items() if len(lst) >= 2]
+    if no_split:
+        assert len(items) == len(rows) and st["merge_indptr"][-1] == 0
+        for k, (r, pb, pe, slot) in enumerate(items):
+            assert owner[k] == r % W
+    else:
+        load = np.zeros(W, int)
+        for k, (r, pb, pe, slot) in enumerate(items):
+            load[owner[k]] += pe - pb
+        assert load.max(initial=0) <= S
+        assert len(items) <= len(rows) + W - 1
+        assert st["merge_indptr"][-1] <= 2 * (W - 1)
+        assert S == max(st["min_seg"], -(-sum(vis) // W))
+        bf = brute_force_items(vis, W, S)
+        got = sorted([(owner[k], r, pb, pe) for k, (r, pb, pe, slot) in enumerate(items)],
+                     key=lambda t: (t[0], t[1]))
+        assert got == bf
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_plan_oracle_invariants_and_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    P = int(rng.choice([1, 3, 16]))
+    causal = bool(rng.integers(0, 2))
+    B = int(rng.integers(0, 12))
+    qo_indptr, kv_indptr, last, qo, kv = _random_case(rng, B, 40, 300, P, causal)
+    Hk = int(rng.choice([1, 2, 8]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    Wd, Wp = int(rng.integers(1, 20)), int(rng.integers(1, 20))
+    ms = int(rng.integers(1, 9))
+    no_split = int(rng.integers(0, 2))
+    decode_only = bool(rng.integers(0, 3) == 0)
+    code, res = pr.plan(None if decode_only else qo_indptr, kv_indptr, last, page_size=P,
+                        num_qo_heads=Hk * G, num_kv_heads=Hk, head_dim=128, causal=causal,
+                        workers_decode=Wd, workers_prefill=Wp, min_seg_pages=ms,
+                        no_split=no_split)
+    assert code == 0, res
+    for st in (res["decode"], res["prefill"]):
+        st["min_seg"] = ms
+        _check_stream(st, no_split)
+    qo_eff = np.ones(B, int) if decode_only else qo
+    assert len(res["decode"]["rows"]) == int((qo_eff == 1).sum())
+    BR = res["prefill"]["BR"]
+    n_tiles = sum(-(-(int(q) * G) // BR) for q in qo_eff if q >= 2)
+    assert len(res["prefill"]["rows"]) == n_tiles
+    # prefill rows: packed-row ranges tile [0, qo*G); causal visibility
+    for (i, rb, re, vp) in res["prefill"]["rows"]:
+        assert 0 <= rb < re <= qo_eff[i] * G and re - rb <= BR
+        vis = kv[i] - qo_eff[i] + (re - 1) // G + 1 if causal else kv[i]
+        assert vp == -(-vis // P)
+    for (i, rb, re, vp) in res["decode"]["rows"]:
+        assert (rb, re) == (0, G) and vp == kv_indptr[i + 1] - kv_indptr[i]
+
+
+def test_tile_size_rule_worked_values():
+    def br(qo_lens, G=4):
+        B = len(qo_lens)
+        kv = [max(q, 1) for q in qo_lens]
+        qo_indptr = np.concatenate([[0], np.cumsum(qo_lens)])
+        kv_indptr = np.arange(B + 1)  # one page each with P = 4096
+        code, res = pr.plan(qo_indptr, kv_indptr, kv, page_size=4096, num_qo_heads=8 * G,
+                            num_kv_heads=8, head_dim=128, causal=True, workers_decode=4,
+                            workers_prefill=4)
+        assert code == 0
+        return res["prefill"]["BR"]
+    assert br([240] * 4) == 128          # mean packed rows 960 -> capped at 128
+    assert br([64]) == 128               # 256 -> 128
+    assert br([3]) == 16                 # 12 -> 16
+    assert br([5, 6]) == 32              # ceil(4 * 11 / 2) = 22 -> 32
+    assert br([1, 1]) == 0               # no prefill request
+
+
+def test_long_request_is_split_into_equal_segments():
+    P = 16
+    kv = np.array([131072] + [1000] * 31)
+    npg = -(-kv // P)
+    kv_indptr = np.concatenate([[0], np.cumsum(npg)])
+    last = kv - (npg - 1) * P
+    code, res = pr.plan(None, kv_indptr, last, page_size=P, num_qo_heads=32, num_kv_heads=8,
+                        head_dim=128, causal=True, workers_decode=128, workers_prefill=1)
+    st = res["decode"]
+    S = st["S"]
+    assert S == -(-int(npg.sum()) // 128)
+    long_items = [it for it in st["items"] if it[0] == 0]
+    assert len(long_items) == -(-8192 // S)
+    assert all(pe - pb == S for (_, pb, pe, _) in long_items[:-1])
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(page_size=0), pr.FI_ERR_INVALID_ARG),
+    (dict(num_qo_heads=6, num_kv_heads=4), pr.FI_ERR_INVALID_ARG),
+    (dict(head_dim=96), pr.FI_ERR_UNSUPPORTED),
+    (dict(num_qo_heads=48, num_kv_heads=3), pr.FI_ERR_UNSUPPORTED),
+    (dict(workers_decode=0), pr.FI_ERR_INVALID_ARG),
+    (dict(min_seg_pages=0), pr.FI_ERR_INVALID_ARG),
+    (dict(br_override=24), pr.FI_ERR_INVALID_ARG),
+    (dict(kv_last_page_len=[0, 3]), pr.FI_ERR_INVALID_ARG),
+    (dict(kv_last_page_len=[5, 3]), pr.FI_ERR_INVALID_ARG),
+    (dict(kv_indptr=[1, 2, 3]), pr.FI_ERR_INVALID_ARG),
+    (dict(kv_indptr=[0, 2, 1]), pr.FI_ERR_INVALID_ARG),
+    (dict(qo_indptr=[0, 9, 10]), pr.FI_ERR_INVALID_ARG),
+    (dict(qo_indptr=[0, 2, 1]), pr.FI_ERR_INVALID_ARG),
+])
+def test_plan_oracle_validation(bad, code):
+    kw = dict(qo_indptr=[0, 2, 3], kv_indptr=[0, 2, 3], kv_last_page_len=[4, 3], page_size=4,
+              num_qo_heads=8, num_kv_heads=2, head_dim=64, causal=True, workers_decode=2,
+              workers_prefill=2)
+    kw.update(bad)
+    got, msg = pr.plan(kw.pop("qo_indptr"), kw.pop("kv_indptr"), kw.pop("kv_last_page_len"), **kw)
+    assert got == code, msg
+
+
+def test_flat_buffer_layout_matches_arrays():
+    qo_indptr = [0, 5, 6, 6, 30]
+    kv_indptr = [0, 2, 5, 5, 12]
+    last = [3, 4, 0, 2]
+    code, res = pr.plan(qo_indptr, kv_indptr, last, page_size=4, num_qo_heads=8, num_kv_heads=2,
+                        head_dim=64, causal=True, workers_decode=3, workers_prefill=5,
+                        min_seg_pages=1)
+    assert code == 0
+    buf = res["buf"]
+    assert buf[0] == pr.MAGIC and buf[2] == len(buf) and buf[4] == 30
+    for at, st in ((pr.STREAM0_AT, res["decode"]), (pr.STREAM1_AT, res["prefill"])):
+        W, nr, ni = buf[at], buf[at + 3], buf[at + 4]
+        assert W == st["W"] and nr == len(st["rows"]) and ni == len(st["items"])
+        o = buf[at + 8]
+        assert [tuple(buf[o + 4 * k:o + 4 * k + 4]) for k in range(nr)] == [tuple(r) for r in st["rows"]]
+        o = buf[at + 9]
+        assert [tuple(buf[o + 4 * k:o + 4 * k + 4]) for k in range(ni)] == [tuple(r) for r in st["items"]]
+        o = buf[at + 10]
+        assert buf[o:o + W + 1] == st["wip"]
