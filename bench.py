@@ -1,0 +1,194 @@
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+One step = the whole path over one batch: the host plan (fi_plan), its upload
+to the device, and the run call (persistent decode kernel + partial merge),
+with inputs resident in HBM.  Default workload: batch decode of the
+Llama-3-8B attention shape (batch 64, 32 query / 8 KV heads, head_dim 128,
+bf16, page 16, kv_len uniform in [512, 4096], random page permutation).
+
+Prints one JSON line.  ``value`` is algorithmic GB/s of the whole step
+(K/V once per KV head for valid tokens, plus Q, O, LSE and index arrays) over
+the step's wall time; ``roofline.achieved`` is the same bytes over the run
+call's average duration measured with HIP events on its stream;
+``cpu_baseline`` times the fp64 oracle on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode HBM GB/s & causal prefill TFLOP/s (bf16), % of MI355X peak"
+HBM_PEAK_GBS = 8000.0
+NUM_CUS = 256
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_bytes(b) -> int:
+    """Algorithmic bytes of one decode pass (the method's own traffic)."""
+    esz = 2 if b.dtype.itemsize == 2 else 4
+    kv = int(b.kv_lens.sum()) * b.num_kv_heads * 2 * b.head_dim * esz
+    qo = 2 * b.total_qo * b.num_qo_heads * b.head_dim * esz
+    lse = b.total_qo * b.num_qo_heads * 4
+    idx = 4 * (len(b.kv_indices) + len(b.kv_indptr) + len(b.kv_last_page_len))
+    return kv + qo + lse + idx
+
+
+def run_decode_bench(args):
+    import torch
+
+    import paged_kv_block_bsr_amd as fi
+    import workloads as wl
+
+    b = getattr(wl, args.workload)()
+    B, Hq, Hk, D, P = b.batch_size, b.num_qo_heads, b.num_kv_heads, b.head_dim, b.page_size
+    wd = args.workers_decode or fi.fi_default_workers(fi.FI_KIND_DECODE, NUM_CUS, Hk)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    ncopy = max(1, args.pool_copies)
+    pools = [b.kv_pool.to(dev) for _ in range(ncopy)]  # rotated so a step cannot hit caches warmed by the last
+    q = b.q.to(dev)
+    i32 = lambda a: torch.from_numpy(np.asarray(a, np.int32)).to(dev)
+    kv_indptr_d, kv_indices_d, last_d = i32(b.kv_indptr), i32(b.kv_indices), i32(b.kv_last_page_len)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    cap_ints, ws_bytes = fi.fi_plan_bounds(B, B, Hq, Hk, D, wd, 1)
+    ws = torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device=dev)
+    pinned = [torch.empty(cap_ints, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    plan_dev = [torch.empty(cap_ints, dtype=torch.int32, device=dev) for _ in range(2)]
+    copied = [torch.cuda.Event() for _ in range(2)]
+    for e in copied:
+        e.record()
+    params = fi.make_params(b.dtype, b.dtype, Hq, Hk, D, P, b.sm_scale, b.soft_cap)
+    kv_indptr_h = np.ascontiguousarray(b.kv_indptr, np.int32)
+    last_h = np.ascontiguousarray(b.kv_last_page_len, np.int32)
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    info = {}
+
+    def step(k, timed_idx=None):
+        j = k % 2
+        copied[j].synchronize()  # the upload that last read this pinned buffer is done
+        plan = fi.fi_plan(None, kv_indptr_h, last_h, page_size=P, num_qo_heads=Hq,
+                          num_kv_heads=Hk, head_dim=D, causal=True, workers_decode=wd,
+                          workers_prefill=1, min_seg_pages=args.min_seg_pages,
+                          out=pinned[j].numpy())
+        info["plan"] = plan
+        plan_dev[j][: plan.ints].copy_(pinned[j][: plan.ints], non_blocking=True)
+        copied[j].record()
+        if timed_idx is not None:
+            starts[timed_idx].record()
+        fi.fi_batch_decode_paged(plan, plan_dev[j], params, q, pools[k % ncopy], kv_indptr_d,
+                                 kv_indices_d, last_d, o, lse, ws)
+        if timed_idx is not None:
+            ends[timed_idx].record()
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(args.warmup + k, k)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    call_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    nbytes = decode_bytes(b)
+    plan = info["plan"]
+    result = {
+        "metric": METRIC,
+        "value": round(nbytes / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if b.dtype.itemsize == 2 else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload, "batch": B, "num_qo_heads": Hq, "num_kv_heads": Hk,
+            "head_dim": D, "page_size": P, "sum_kv_len": int(b.kv_lens.sum()),
+            "pool_pages": b.pool_pages, "workers_decode": wd,
+            "decode_items": int(plan.info.decode_items), "decode_slots": int(plan.info.decode_slots),
+            "algorithmic_bytes_per_step": nbytes,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(nbytes / (call_ms * 1e-3) / 1e9, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(nbytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel_ms": round(call_ms, 5),
+            "kernel": "decode_kernel + merge_partials_kernel (one fi_batch_decode_paged call)",
+        },
+    }
+    return result, b, nbytes
+
+
+def cpu_baseline(b, nbytes, budget_s=12.0):
+    """The fp64 oracle on the host cores over the whole batch (the sample)."""
+    from oracle import attn as ref
+
+    q64 = b.q.double().numpy()
+    pool64 = b.kv_pool.double().numpy()
+    kw = dict(page_size=b.page_size, num_qo_heads=b.num_qo_heads, num_kv_heads=b.num_kv_heads,
+              head_dim=b.head_dim, causal=b.causal, sm_scale=b.sm_scale, soft_cap=b.soft_cap)
+    times = []
+    while True:
+        t0 = time.perf_counter()
+        ref.attention(q64, pool64, b.qo_indptr, b.kv_indptr, b.kv_indices, b.kv_last_page_len, **kw)
+        times.append(time.perf_counter() - t0)
+        log(f"[bench] oracle pass {len(times)}: {times[-1]:.2f} s")
+        if sum(times) >= budget_s or len(times) >= 30:
+            break
+    t = float(np.mean(times))
+    return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": ref.num_threads(),
+            "kind": "oracle",
+            "sample": f"whole {b.name} batch (all {b.total_qo * b.num_qo_heads} query rows), "
+                      f"{len(times)} passes, mean {t:.2f} s per pass"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama8b_decode",
+                    choices=["llama8b_decode", "skewed_long_decode", "tiny_decode_fp32"])
+    ap.add_argument("--workers-decode", type=int, default=0)
+    ap.add_argument("--min-seg-pages", type=int, default=8)
+    ap.add_argument("--pool-copies", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+    result, b, nbytes = run_decode_bench(args)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(b, nbytes)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

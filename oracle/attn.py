@@ -32,6 +32,7 @@ def lib():
                 _build.build()
             L = ctypes.CDLL(_build.LIB)
             L.oref_last_error.restype = ctypes.c_char_p
+            L.oref_num_threads.restype = ctypes.c_int
             L.oref_validate.restype = ctypes.c_int
             L.oref_validate.argtypes = [ctypes.c_int, _i32p, _i32p, _i32p, _i32p, ctypes.c_int,
                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -58,6 +59,11 @@ def lib():
 
 class OracleError(ValueError):
     pass
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle runs with."""
+    return int(lib().oref_num_threads())
 
 
 def _i32(a):

@@ -52,6 +52,19 @@ static char g_err[256];
 
 const char *oref_last_error(void) { return g_err; }
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads the oracle's parallel loops use. */
+int oref_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
 static int fail(const char *msg, long long a, long long b) {
   snprintf(g_err, sizeof(g_err), "%s (%lld, %lld)", msg, a, b);
   return OREF_EINVAL;

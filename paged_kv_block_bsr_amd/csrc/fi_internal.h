@@ -1,0 +1,54 @@
+// fi_internal.h -- host-side internals shared by the library's translation
+// units: the thread-local error message and the kernel launch entry points.
+#pragma once
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "fi.h"
+
+namespace fi {
+
+// Records a printf-style message for fi_last_error() and returns `code`.
+int set_error(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+int build_plan(const fi_plan_in* in, int32_t* buf, int64_t capacity, fi_plan_info* info);
+int plan_bounds(int32_t B, int64_t total_qo, int32_t Hq, int32_t Hk, int32_t D, int32_t Wd,
+                int32_t Wp, int64_t* plan_ints, int64_t* ws_bytes);
+
+// Everything a kernel of one stream needs; built by the API layer after
+// validation.  Device pointers unless noted.
+struct RunArgs {
+  const int32_t* plan;          // device plan
+  const void* q;
+  const void* kv_pool;
+  int64_t pool_pages;
+  const int32_t* qo_indptr;     // NULL: request i has query row i
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  const int32_t* kv_last_page_len;
+  void* o;                      // direct outputs
+  float* lse;                   // may be NULL
+  float* ws;                    // float workspace base
+  int32_t Hq, Hk, D, P, G;
+  int32_t causal;
+  float sm_scale;
+  float soft_cap;
+  fi_dtype dtype, out_dtype;
+  int32_t workers;              // grid.x of this stream's kernel
+  int32_t max_tasks;            // merge kernel: grid.x bound (W - 1)
+  int32_t stream_at;            // H_STREAM0 or H_STREAM1
+  void* hip_stream;
+};
+
+// Kernel launches; return FI_OK or FI_ERR_*.  Each validates nothing: the
+// API layer has already checked shapes, dtypes and the plan.
+int launch_decode(const RunArgs& a);
+int launch_prefill(const RunArgs& a);
+int launch_merge_partials(const RunArgs& a);
+int launch_merge_state(const void* va, const float* sa, const void* vb, const float* sb,
+                       void* vo, float* so, int64_t n_rows, int32_t head_dim, fi_dtype vdt,
+                       fi_dtype odt, void* stream);
+
+}  // namespace fi

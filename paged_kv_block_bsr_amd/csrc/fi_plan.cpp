@@ -1,0 +1,326 @@
+// fi_plan.cpp -- the CPU-side inspector: splits each step's KV page stream
+// into equal segments, one per persistent worker, and records where partial
+// results go (FlashInfer paper page, "Load balancing that survives CUDA
+// graphs"; talk page, "Runtime Scheduler for Dynamic Problem Shapes": a cost
+// model inspected ahead of time, deterministic balance, no tail wave).
+//
+// Cost model: one unit per visible KV page of a row.  Rows are decode rows
+// (one query token, the G heads of a KV head packed together) and prefill
+// tiles of BR packed (token, head) rows; BR follows the batch's mean packed
+// query length (paper page, the query tile size of the JIT paragraph).  The
+// two kinds form separate streams because they run in different kernels.
+//
+// Host only: no HIP call.  O(B + rows + items + W) time.
+#include <climits>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "fi.h"
+#include "fi_internal.h"
+#include "plan_format.h"
+
+namespace fi {
+namespace {
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline int32_t next_pow2(int64_t x) {
+  int64_t p = 1;
+  while (p < x) p <<= 1;
+  return (int32_t)p;
+}
+
+inline int64_t align64(int64_t n) { return ceil_div(n, 64) * 64; }
+
+struct Row {
+  int32_t req, rb, re, vis;
+};
+
+struct StreamPlan {
+  int32_t W = 1, S = 1, tile = 0;
+  std::vector<Row> rows;
+  // items in final order
+  std::vector<int32_t> item_row, item_pb, item_pe, item_slot, wip, merge, split;
+};
+
+void partition(StreamPlan& st, int32_t min_seg, bool no_split) {
+  const int32_t W = st.W;
+  const int64_t nrows = (int64_t)st.rows.size();
+  int64_t C = 0;
+  for (const Row& r : st.rows) C += r.vis;
+  st.S = (int32_t)std::max<int64_t>(min_seg, ceil_div(C, W));
+  const int64_t S = st.S;
+  st.wip.assign(W + 1, 0);
+  st.merge.assign(nrows + 1, 0);
+  std::vector<int32_t> nitems_row(nrows, 0);
+
+  if (no_split) {
+    // one item per row on worker r mod W: counting sort by worker keeps rows ascending
+    for (int64_t r = 0; r < nrows; ++r) st.wip[r % W + 1] += 1;
+    for (int32_t w = 0; w < W; ++w) st.wip[w + 1] += st.wip[w];
+    const int64_t n = nrows;
+    st.item_row.assign(n, 0);
+    st.item_pb.assign(n, 0);
+    st.item_pe.assign(n, 0);
+    st.item_slot.assign(n, -1);
+    std::vector<int32_t> fill(st.wip.begin(), st.wip.end() - 1);
+    for (int64_t r = 0; r < nrows; ++r) {
+      int32_t k = fill[r % W]++;
+      st.item_row[k] = (int32_t)r;
+      st.item_pe[k] = st.rows[r].vis;
+    }
+    return;  // merge stays all-zero, no split rows
+  }
+
+  // Rows in order, each cut at worker boundaries: the generated order is
+  // already sorted by (worker, row) because worker indices never decrease.
+  int64_t c = 0;
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int64_t vis = st.rows[r].vis;
+    if (vis == 0) {
+      int64_t w = std::min<int64_t>(c / S, W - 1);
+      st.item_row.push_back((int32_t)r);
+      st.item_pb.push_back(0);
+      st.item_pe.push_back(0);
+      st.wip[w + 1] += 1;
+      nitems_row[r] = 1;
+    } else {
+      for (int64_t w = c / S; w <= (c + vis - 1) / S; ++w) {
+        int64_t lo = std::max<int64_t>(c, w * S), hi = std::min<int64_t>(c + vis, (w + 1) * S);
+        st.item_row.push_back((int32_t)r);
+        st.item_pb.push_back((int32_t)(lo - c));
+        st.item_pe.push_back((int32_t)(hi - c));
+        st.wip[w + 1] += 1;
+        nitems_row[r] += 1;
+      }
+    }
+    c += vis;
+  }
+  for (int32_t w = 0; w < W; ++w) st.wip[w + 1] += st.wip[w];
+  // slots: rows with k >= 2 items get k consecutive slots, in page order
+  for (int64_t r = 0; r < nrows; ++r) {
+    int32_t k = nitems_row[r];
+    st.merge[r + 1] = st.merge[r] + (k >= 2 ? k : 0);
+    if (k >= 2) st.split.push_back((int32_t)r);
+  }
+  st.item_slot.assign(st.item_row.size(), -1);
+  int32_t prev_row = -1, j = 0;
+  for (size_t k = 0; k < st.item_row.size(); ++k) {
+    int32_t r = st.item_row[k];
+    j = (r == prev_row) ? j + 1 : 0;
+    prev_row = r;
+    if (nitems_row[r] >= 2) st.item_slot[k] = st.merge[r] + j;
+  }
+}
+
+int validate(const fi_plan_in& in) {
+  const int B = in.batch_size;
+  if (B < 0) return set_error(FI_ERR_INVALID_ARG, "fi_plan: batch_size < 0");
+  if (in.page_size < 1) return set_error(FI_ERR_INVALID_ARG, "fi_plan: page_size < 1");
+  if (in.num_qo_heads < 1 || in.num_kv_heads < 1 || in.num_qo_heads % in.num_kv_heads)
+    return set_error(FI_ERR_INVALID_ARG, "fi_plan: num_qo_heads must be a multiple of num_kv_heads");
+  if (in.head_dim != 64 && in.head_dim != 128)
+    return set_error(FI_ERR_UNSUPPORTED, "fi_plan: head_dim must be 64 or 128");
+  const int G = in.num_qo_heads / in.num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return set_error(FI_ERR_UNSUPPORTED, "fi_plan: group size must be 1, 2, 4 or 8");
+  if (in.workers_decode < 1 || in.workers_prefill < 1)
+    return set_error(FI_ERR_INVALID_ARG, "fi_plan: workers must be >= 1");
+  if (in.min_seg_pages < 1) return set_error(FI_ERR_INVALID_ARG, "fi_plan: min_seg_pages < 1");
+  if (in.br_override != 0 && in.br_override != 16 && in.br_override != 32 &&
+      in.br_override != 64 && in.br_override != 128)
+    return set_error(FI_ERR_INVALID_ARG, "fi_plan: br_override must be 0, 16, 32, 64 or 128");
+  if (in.no_split != 0 && in.no_split != 1) return set_error(FI_ERR_INVALID_ARG, "fi_plan: no_split");
+  if (B > 0 && (!in.kv_indptr || !in.kv_last_page_len))
+    return set_error(FI_ERR_INVALID_ARG, "fi_plan: null index array");
+  if (B == 0 && !in.kv_indptr) return set_error(FI_ERR_INVALID_ARG, "fi_plan: null kv_indptr");
+  if (in.kv_indptr[0] != 0) return set_error(FI_ERR_INVALID_ARG, "fi_plan: kv_indptr[0] != 0");
+  if (in.qo_indptr && in.qo_indptr[0] != 0) return set_error(FI_ERR_INVALID_ARG, "fi_plan: qo_indptr[0] != 0");
+  for (int i = 0; i < B; ++i) {
+    int64_t np = (int64_t)in.kv_indptr[i + 1] - in.kv_indptr[i];
+    if (np < 0) return set_error(FI_ERR_INVALID_ARG, "fi_plan: kv_indptr decreases at %d", i);
+    int64_t qo = in.qo_indptr ? (int64_t)in.qo_indptr[i + 1] - in.qo_indptr[i] : 1;
+    if (qo < 0) return set_error(FI_ERR_INVALID_ARG, "fi_plan: qo_indptr decreases at %d", i);
+    int32_t last = in.kv_last_page_len[i];
+    if (np > 0 && (last < 1 || last > in.page_size))
+      return set_error(FI_ERR_INVALID_ARG, "fi_plan: kv_last_page_len[%d] = %d not in [1, %d]", i,
+                       last, in.page_size);
+    int64_t kv = np == 0 ? 0 : (np - 1) * in.page_size + last;
+    if (kv > INT32_MAX) return set_error(FI_ERR_INVALID_ARG, "fi_plan: kv_len of request %d too large", i);
+    if (in.causal && qo >= 2 && qo > kv)
+      return set_error(FI_ERR_INVALID_ARG, "fi_plan: causal request %d has qo_len %lld > kv_len %lld",
+                       i, (long long)qo, (long long)kv);
+  }
+  return FI_OK;
+}
+
+// Float workspace regions (float units, each padded to 64 floats = 256 B):
+// decode partial o, decode partial lse, prefill partial o, prefill partial lse.
+void ws_layout(int32_t Hq, int32_t Hk, int32_t D, int32_t Wd, int32_t Wp, int64_t off[4],
+               int64_t* total) {
+  int64_t cap_d = 2 * (int64_t)(Wd - 1), cap_p = 2 * (int64_t)(Wp - 1);
+  int64_t sz[4] = {align64(cap_d * Hq * D), align64(cap_d * Hq),
+                   align64(cap_p * Hk * kMaxTileRows * D), align64(cap_p * Hk * kMaxTileRows)};
+  off[0] = 0;
+  off[1] = sz[0];
+  off[2] = sz[0] + sz[1];
+  off[3] = sz[0] + sz[1] + sz[2];
+  *total = sz[0] + sz[1] + sz[2] + sz[3];
+}
+
+}  // namespace
+
+int plan_bounds(int32_t B, int64_t total_qo, int32_t Hq, int32_t Hk, int32_t D, int32_t Wd,
+                int32_t Wp, int64_t* plan_ints, int64_t* ws_bytes) {
+  if (B < 0 || total_qo < 0 || Hq < 1 || Hk < 1 || Hq % Hk || D < 1 || Wd < 1 || Wp < 1)
+    return set_error(FI_ERR_INVALID_ARG, "fi_plan_bounds: bad arguments");
+  const int64_t G = Hq / Hk;
+  const int64_t rows_d = B;
+  const int64_t rows_p = ceil_div(total_qo * G, 16) + B;
+  auto stream_ints = [](int64_t rows, int64_t W) {
+    int64_t items = rows + W - 1;
+    return 4 * rows + 4 * items + (W + 1) + (rows + 1) + rows;
+  };
+  if (plan_ints) *plan_ints = kHeaderInts + stream_ints(rows_d, Wd) + stream_ints(rows_p, Wp);
+  int64_t off[4], total;
+  ws_layout(Hq, Hk, D, Wd, Wp, off, &total);
+  if (ws_bytes) *ws_bytes = total * 4;
+  return FI_OK;
+}
+
+int build_plan(const fi_plan_in* inp, int32_t* buf, int64_t capacity, fi_plan_info* info) {
+  clear_error();
+  if (!inp) return set_error(FI_ERR_INVALID_ARG, "fi_plan: null input");
+  const fi_plan_in& in = *inp;
+  int rc = validate(in);
+  if (rc) return rc;
+  const int B = in.batch_size, P = in.page_size;
+  const int32_t Hq = in.num_qo_heads, Hk = in.num_kv_heads, D = in.head_dim;
+  const int32_t G = Hq / Hk;
+
+  // P2 / P3 / P4
+  std::vector<int64_t> np(B), kv(B), qo(B);
+  int64_t total_qo = 0, sum_prefill_qo = 0, n_prefill = 0;
+  for (int i = 0; i < B; ++i) {
+    np[i] = (int64_t)in.kv_indptr[i + 1] - in.kv_indptr[i];
+    kv[i] = np[i] == 0 ? 0 : (np[i] - 1) * P + in.kv_last_page_len[i];
+    qo[i] = in.qo_indptr ? (int64_t)in.qo_indptr[i + 1] - in.qo_indptr[i] : 1;
+    total_qo += qo[i];
+    if (qo[i] >= 2) {
+      sum_prefill_qo += qo[i];
+      n_prefill += 1;
+    }
+  }
+  int32_t BR = 0;
+  if (in.br_override) {
+    BR = in.br_override;
+  } else if (n_prefill) {
+    int64_t mean = ceil_div((int64_t)G * sum_prefill_qo, n_prefill);
+    BR = std::min<int32_t>(kMaxTileRows, std::max<int32_t>(16, next_pow2(mean)));
+  }
+  if (total_qo > INT32_MAX) return set_error(FI_ERR_INVALID_ARG, "fi_plan: too many queries");
+
+  // P5
+  StreamPlan st[2];
+  st[0].W = in.workers_decode;
+  st[0].tile = G;
+  st[1].W = in.workers_prefill;
+  st[1].tile = BR;
+  for (int i = 0; i < B; ++i) {
+    if (qo[i] == 1) {
+      st[0].rows.push_back({i, 0, G, (int32_t)np[i]});
+    } else if (qo[i] >= 2) {
+      const int64_t npk = qo[i] * G;
+      for (int64_t rb = 0; rb < npk; rb += BR) {
+        int64_t re = std::min<int64_t>(rb + BR, npk);
+        int64_t tok_hi = (re - 1) / G;
+        int64_t vis = in.causal ? kv[i] - qo[i] + tok_hi + 1 : kv[i];
+        st[1].rows.push_back({i, (int32_t)rb, (int32_t)re, (int32_t)ceil_div(vis, P)});
+      }
+    }
+  }
+  // P6 - P8
+  for (auto& s : st) partition(s, in.min_seg_pages, in.no_split != 0);
+
+  int64_t off[4], ws_total;
+  ws_layout(Hq, Hk, D, in.workers_decode, in.workers_prefill, off, &ws_total);
+  if (ws_total > INT32_MAX)
+    return set_error(FI_ERR_INVALID_ARG, "fi_plan: float workspace too large for these workers");
+
+  // P9: size, then emit
+  int64_t need = kHeaderInts;
+  for (auto& s : st)
+    need += 4 * (int64_t)s.rows.size() + 4 * (int64_t)s.item_row.size() + (s.W + 1) +
+            ((int64_t)s.rows.size() + 1) + (int64_t)s.split.size();
+  if (!buf || capacity < need)
+    return set_error(FI_ERR_WORKSPACE_TOO_SMALL, "fi_plan: plan buffer holds %lld ints, needs %lld",
+                     (long long)capacity, (long long)need);
+  if (need > INT32_MAX) return set_error(FI_ERR_INVALID_ARG, "fi_plan: plan too large");
+  std::memset(buf, 0, sizeof(int32_t) * kHeaderInts);
+  int64_t pos = kHeaderInts;
+  for (int k = 0; k < 2; ++k) {
+    StreamPlan& s = st[k];
+    int32_t* d = buf + (k == 0 ? H_STREAM0 : H_STREAM1);
+    const int64_t nr = (int64_t)s.rows.size(), ni = (int64_t)s.item_row.size();
+    d[S_W] = s.W;
+    d[S_SEG] = s.S;
+    d[S_TILE] = s.tile;
+    d[S_NROWS] = (int32_t)nr;
+    d[S_NITEMS] = (int32_t)ni;
+    d[S_NSLOTS] = s.merge.back();
+    d[S_NSPLIT] = (int32_t)s.split.size();
+    d[S_SLOTCAP] = 2 * (s.W - 1);
+    d[S_WS_O] = (int32_t)off[k == 0 ? 0 : 2];
+    d[S_WS_LSE] = (int32_t)off[k == 0 ? 1 : 3];
+    d[S_KIND] = k;
+    d[S_OFF_ROWS] = (int32_t)pos;
+    for (const Row& r : s.rows) {
+      buf[pos++] = r.req;
+      buf[pos++] = r.rb;
+      buf[pos++] = r.re;
+      buf[pos++] = r.vis;
+    }
+    d[S_OFF_ITEMS] = (int32_t)pos;
+    for (int64_t j = 0; j < ni; ++j) {
+      buf[pos++] = s.item_row[j];
+      buf[pos++] = s.item_pb[j];
+      buf[pos++] = s.item_pe[j];
+      buf[pos++] = s.item_slot[j];
+    }
+    d[S_OFF_WIP] = (int32_t)pos;
+    for (int32_t v : s.wip) buf[pos++] = v;
+    d[S_OFF_MERGE] = (int32_t)pos;
+    for (int32_t v : s.merge) buf[pos++] = v;
+    d[S_OFF_SPLIT] = (int32_t)pos;
+    for (int32_t v : s.split) buf[pos++] = v;
+  }
+  buf[H_MAGIC] = kPlanMagic;
+  buf[H_VERSION] = kPlanVersion;
+  buf[H_SIZE] = (int32_t)pos;
+  buf[H_BATCH] = B;
+  buf[H_TOTAL_QO] = (int32_t)total_qo;
+  buf[H_HQ] = Hq;
+  buf[H_HK] = Hk;
+  buf[H_D] = D;
+  buf[H_PAGE] = P;
+  buf[H_CAUSAL] = in.causal ? 1 : 0;
+  buf[H_GROUP] = G;
+  buf[H_WS_FLOATS] = (int32_t)ws_total;
+  if (info) {
+    info->plan_ints = pos;
+    info->float_ws_bytes = ws_total * 4;
+    info->decode_rows = (int32_t)st[0].rows.size();
+    info->decode_items = (int32_t)st[0].item_row.size();
+    info->decode_slots = st[0].merge.back();
+    info->decode_segment_pages = st[0].S;
+    info->prefill_rows = (int32_t)st[1].rows.size();
+    info->prefill_items = (int32_t)st[1].item_row.size();
+    info->prefill_slots = st[1].merge.back();
+    info->prefill_segment_pages = st[1].S;
+    info->prefill_tile_rows = BR;
+  }
+  return FI_OK;
+}
+
+}  // namespace fi

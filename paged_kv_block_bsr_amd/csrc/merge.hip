@@ -1,0 +1,160 @@
+// merge.hip -- log-sum-exp composition of attention states (gfx950).
+//
+// merge_partials: for every row the plan split over k >= 2 workers, combine
+// the k partial (o, lse) slots into the final output (serving-engine page,
+// "FlashDecoding: Parallel KV Split", the merge step; paper page, partial
+// results merged with the log-sum-exp composition).  Fixed grid
+// (workers - 1, KV heads): block x takes the x-th split row of the stream,
+// or exits when there is none, so the launch shape never depends on the
+// batch.
+//
+// merge_state: the two-way merge of the cascade (serving-engine page,
+// "Cascade Attention for Shared Prefixes", merge_state).
+#include "device_common.h"
+#include "fi_internal.h"
+
+namespace fi {
+namespace {
+
+constexpr int kThreads = 256;
+
+struct MergeParams {
+  const int32_t* plan;
+  const int32_t* qo_indptr;
+  uint8_t* o;
+  float* lse;
+  const float* ws;
+  int32_t Hq, Hk, D, G;
+  int32_t stream_at;
+  int32_t out_bf16;
+};
+
+__global__ __launch_bounds__(kThreads) void merge_partials_kernel(MergeParams a) {
+  const int32_t* sd = a.plan + a.stream_at;
+  const int task = blockIdx.x;
+  if (task >= sd[S_NSPLIT]) return;
+  const int g = blockIdx.y;
+  const int32_t* rows = a.plan + sd[S_OFF_ROWS];
+  const int32_t* merge = a.plan + sd[S_OFF_MERGE];
+  const int row = a.plan[sd[S_OFF_SPLIT] + task];
+  const int req = rows[4 * row + 0];
+  const int rb = rows[4 * row + 1];
+  const int re = rows[4 * row + 2];
+  const int s0 = merge[row], s1 = merge[row + 1];
+  // partial layout [slot][Hk][stride][D]; stride = G for decode rows, 128 for tiles
+  const int stride = sd[S_KIND] == 0 ? a.G : kMaxTileRows;
+  const float* wo = a.ws + sd[S_WS_O];
+  const float* wl = a.ws + sd[S_WS_LSE];
+  const int qbase = a.qo_indptr ? a.qo_indptr[req] : req;
+  const int D = a.D, G = a.G;
+  const int n = (re - rb) * D;
+  for (int idx = threadIdx.x; idx < n; idx += kThreads) {
+    const int r = idx / D, d = idx % D;
+    const int packed = rb + r;
+    float M = neg_inf();
+    for (int s = s0; s < s1; ++s) M = fmaxf(M, wl[((int64_t)s * a.Hk + g) * stride + r]);
+    float out = 0.f, lse = neg_inf();
+    if (M != neg_inf()) {
+      float L = 0.f, O = 0.f;
+      for (int s = s0; s < s1; ++s) {
+        const int64_t pr = ((int64_t)s * a.Hk + g) * stride + r;
+        const float w = __expf(wl[pr] - M);
+        L += w;
+        O += w * wo[pr * D + d];
+      }
+      out = O / L;
+      lse = M + __logf(L);
+    }
+    const int64_t orow = (int64_t)(qbase + packed / G) * a.Hq + g * G + packed % G;
+    if (a.out_bf16)
+      reinterpret_cast<uint16_t*>(a.o)[orow * D + d] = (uint16_t)f32_to_bf16_bits(out);
+    else
+      reinterpret_cast<float*>(a.o)[orow * D + d] = out;
+    if (a.lse && d == 0) a.lse[orow] = lse;
+  }
+}
+
+// Two-way merge; one wave per row, lane e takes elements e, e + 64, ...  Every
+// lane reads both lse values in the same instruction, before any lane writes,
+// so the outputs may alias the inputs.
+template <typename VT, typename OT>
+__global__ __launch_bounds__(kThreads) void merge_state_kernel(const uint8_t* va, const float* sa,
+                                                               const uint8_t* vb, const float* sb,
+                                                               uint8_t* vo, float* so,
+                                                               int64_t n_rows, int32_t D) {
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * (kThreads / 64);
+  for (int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); row < n_rows;
+       row += waves) {
+    const float la = sa[row], lb = sb[row];
+    const float M = fmaxf(la, lb);
+    const bool empty = M == neg_inf();
+    const float wa = empty ? 0.f : __expf(la - M);
+    const float wb = empty ? 0.f : __expf(lb - M);
+    const float inv = empty ? 0.f : 1.f / (wa + wb);
+    for (int e = lane; e < D; e += 64) {
+      const int64_t i = row * D + e;
+      float x, y;
+      if constexpr (VT::kBytes == 2) {
+        x = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(va)[i] << 16);
+        y = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(vb)[i] << 16);
+      } else {
+        x = reinterpret_cast<const float*>(va)[i];
+        y = reinterpret_cast<const float*>(vb)[i];
+      }
+      const float r = empty ? 0.f : (wa * x + wb * y) * inv;
+      if constexpr (OT::kBytes == 2)
+        reinterpret_cast<uint16_t*>(vo)[i] = (uint16_t)f32_to_bf16_bits(r);
+      else
+        reinterpret_cast<float*>(vo)[i] = r;
+    }
+    if (lane == 0) so[row] = empty ? neg_inf() : M + __logf(wa + wb);
+  }
+}
+
+}  // namespace
+
+int launch_merge_partials(const RunArgs& r) {
+  MergeParams p;
+  p.plan = r.plan;
+  p.qo_indptr = r.qo_indptr;
+  p.o = static_cast<uint8_t*>(r.o);
+  p.lse = r.lse;
+  p.ws = r.ws;
+  p.Hq = r.Hq;
+  p.Hk = r.Hk;
+  p.D = r.D;
+  p.G = r.G;
+  p.stream_at = r.stream_at;
+  p.out_bf16 = r.out_dtype == FI_BF16;
+  dim3 grid(std::max(1, r.max_tasks), r.Hk), block(kThreads);
+  hipLaunchKernelGGL(merge_partials_kernel, grid, block, 0, (hipStream_t)r.hip_stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(FI_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
+  return FI_OK;
+}
+
+int launch_merge_state(const void* va, const float* sa, const void* vb, const float* sb, void* vo,
+                       float* so, int64_t n_rows, int32_t head_dim, fi_dtype vdt, fi_dtype odt,
+                       void* stream) {
+  if (n_rows == 0) return FI_OK;
+  const int64_t blocks = std::min<int64_t>((n_rows + kThreads / 64 - 1) / (kThreads / 64), 65536);
+  dim3 grid((unsigned)blocks), block(kThreads);
+  auto* A = static_cast<const uint8_t*>(va);
+  auto* Bv = static_cast<const uint8_t*>(vb);
+  auto* O = static_cast<uint8_t*>(vo);
+  hipStream_t s = (hipStream_t)stream;
+  if (vdt == FI_BF16 && odt == FI_BF16)
+    hipLaunchKernelGGL((merge_state_kernel<BF16, BF16>), grid, block, 0, s, A, sa, Bv, sb, O, so, n_rows, head_dim);
+  else if (vdt == FI_F32 && odt == FI_BF16)
+    hipLaunchKernelGGL((merge_state_kernel<F32, BF16>), grid, block, 0, s, A, sa, Bv, sb, O, so, n_rows, head_dim);
+  else if (vdt == FI_F32 && odt == FI_F32)
+    hipLaunchKernelGGL((merge_state_kernel<F32, F32>), grid, block, 0, s, A, sa, Bv, sb, O, so, n_rows, head_dim);
+  else
+    return set_error(FI_ERR_UNSUPPORTED, "merge_state: dtype combination");
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(FI_ERR_HIP, "merge_state launch: %s", hipGetErrorString(e));
+  return FI_OK;
+}
+
+}  // namespace fi

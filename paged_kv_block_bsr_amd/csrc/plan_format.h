@@ -1,0 +1,68 @@
+// plan_format.h -- layout of the int32 plan buffer that fi_plan writes and the
+// kernels read from device memory.
+//
+// The buffer starts with a fixed header, then per stream (0 = decode rows,
+// 1 = prefill tiles) five arrays:
+//   rows   [n_rows][4]  {request, packed_row_begin, packed_row_end, visible_pages}
+//   items  [n_items][4] {row, page_begin, page_end, slot}  (slot -1: write the
+//                        output directly; else the partial-result slot)
+//   wip    [W+1]        items of worker w are items[wip[w] .. wip[w+1])
+//   merge  [n_rows+1]   slots of row r are merge[r] .. merge[r+1]
+//   split  [n_split]    rows with two or more items, in row order
+// A packed row r of a request stands for (token r / G, head-in-group r % G);
+// a decode row packs the G query heads of one KV head.  Page indices in
+// items are local to the request (the kernel adds kv_indptr[request]).
+//
+// The float workspace holds, per stream, partial outputs [slot_cap][Hk][tile][D]
+// and partial lse [slot_cap][Hk][tile] (fp32, natural log) at the float offsets
+// recorded in the stream descriptor; tile = G for decode, 128 for prefill.
+#pragma once
+#include <stdint.h>
+
+namespace fi {
+
+constexpr int32_t kPlanMagic = 0x31504946;  // "FIP1"
+constexpr int32_t kPlanVersion = 1;
+constexpr int kHeaderInts = 64;
+constexpr int kMaxTileRows = 128;
+
+// header words
+enum : int {
+  H_MAGIC = 0,
+  H_VERSION = 1,
+  H_SIZE = 2,
+  H_BATCH = 3,
+  H_TOTAL_QO = 4,
+  H_HQ = 5,
+  H_HK = 6,
+  H_D = 7,
+  H_PAGE = 8,
+  H_CAUSAL = 9,
+  H_GROUP = 10,
+  H_WS_FLOATS = 11,
+  H_STREAM0 = 12,
+  H_STREAM1 = 32,
+};
+
+// stream descriptor words (relative to H_STREAM0 / H_STREAM1)
+enum : int {
+  S_W = 0,
+  S_SEG = 1,
+  S_TILE = 2,
+  S_NROWS = 3,
+  S_NITEMS = 4,
+  S_NSLOTS = 5,
+  S_NSPLIT = 6,
+  S_SLOTCAP = 7,
+  S_OFF_ROWS = 8,
+  S_OFF_ITEMS = 9,
+  S_OFF_WIP = 10,
+  S_OFF_MERGE = 11,
+  S_OFF_SPLIT = 12,
+  S_WS_O = 13,
+  S_WS_LSE = 14,
+  S_KIND = 15,
+  kStreamDescInts = 20,
+};
+
+}  // namespace fi

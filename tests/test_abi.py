@@ -1,0 +1,180 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+- libfi.so loads and exports every function include/fi.h declares;
+- fi_plan (C++) equals the plan oracle (pure Python) bit-exactly on every
+  int32 word, over seeded random batches and the named workloads;
+- error codes for invalid inputs, plan capacity, fi_plan_bounds.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import paged_kv_block_bsr_amd as fi
+import workloads
+from oracle import plan_ref as pr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "fi.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fi_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 10
+    L = fi.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(fi.EXPORTS)
+    assert fi.fi_version() >= 100
+
+
+def test_default_workers():
+    assert fi.fi_default_workers(fi.FI_KIND_DECODE, 256, 8) >= 1
+    assert fi.fi_default_workers(fi.FI_KIND_PREFILL, 256, 8) >= 1
+    assert fi.fi_default_workers(fi.FI_KIND_DECODE, 0, 8) == 1
+
+
+def _compare(qo_indptr, kv_indptr, last, **kw):
+    code, res = pr.plan(qo_indptr, kv_indptr, last, **kw)
+    assert code == 0, res
+    plan = fi.fi_plan(qo_indptr, kv_indptr, last, **kw)
+    got = plan.buf[:plan.ints]
+    assert plan.ints == len(res["buf"])
+    assert np.array_equal(got, np.asarray(res["buf"], np.int32))
+    d = fi.decode_plan_buffer(got)
+    for name in ("decode", "prefill"):
+        st = res[name]
+        assert d[name]["rows"] == [tuple(r) for r in st["rows"]]
+        assert d[name]["items"] == [tuple(r) for r in st["items"]]
+        assert d[name]["wip"] == st["wip"]
+        assert d[name]["merge_indptr"] == st["merge_indptr"]
+        assert d[name]["split_rows"] == st["split_rows"]
+    assert plan.float_ws_bytes == 4 * res["ws_floats"]
+    return plan, res
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_fi_plan_bit_exact_vs_oracle_random(seed):
+    rng = np.random.default_rng(1000 + seed)
+    P = int(rng.choice([1, 3, 16, 32]))
+    causal = bool(rng.integers(0, 2))
+    B = int(rng.integers(0, 20))
+    qo = rng.integers(0, 70, size=B)
+    kv = np.array([rng.integers(q if (causal and q >= 2) else 0, max(q, 600) + 1) for q in qo],
+                  dtype=np.int64)
+    npg = -(-kv // P)
+    last = np.where(npg > 0, kv - (npg - 1) * P, 0).astype(np.int32)
+    kv_indptr = np.concatenate([[0], np.cumsum(npg)]).astype(np.int32)
+    qo_indptr = np.concatenate([[0], np.cumsum(qo)]).astype(np.int32)
+    Hk = int(rng.choice([1, 2, 8]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    decode_only = bool(rng.integers(0, 3) == 0)
+    _compare(None if decode_only else qo_indptr, kv_indptr, last, page_size=P,
+             num_qo_heads=Hk * G, num_kv_heads=Hk, head_dim=int(rng.choice([64, 128])),
+             causal=causal, workers_decode=int(rng.integers(1, 40)),
+             workers_prefill=int(rng.integers(1, 40)), min_seg_pages=int(rng.integers(1, 10)),
+             br_override=int(rng.choice([0, 0, 16, 64])), no_split=int(rng.integers(0, 2)))
+
+
+@pytest.mark.parametrize("name", ["tiny_decode_fp32", "llama8b_decode", "skewed_long_decode",
+                                  "mixed_ragged_step"])
+def test_fi_plan_bit_exact_on_named_workloads(name, monkeypatch):
+    # only the index arrays matter: build them without drawing the pools
+    rng = np.random.default_rng(7)
+    if name == "tiny_decode_fp32":
+        kv, qo, P, Hq, Hk, D = np.array([17, 64, 100, 3]), None, 16, 8, 2, 64
+    elif name == "llama8b_decode":
+        kv, qo, P, Hq, Hk, D = rng.integers(512, 4097, 64), None, 16, 32, 8, 128
+    elif name == "skewed_long_decode":
+        kv = np.concatenate([[131072], np.clip(np.rint(np.exp(rng.normal(np.log(1024), 1, 31))), 128, 4096)]).astype(np.int64)
+        qo, P, Hq, Hk, D = None, 16, 32, 8, 128
+    else:
+        qp = rng.choice([64, 128, 256, 512], 16)
+        kv = np.concatenate([rng.integers(0, 2049, 16) + qp, rng.integers(256, 8193, 48)])
+        qo = np.concatenate([[0], np.cumsum(np.concatenate([qp, np.ones(48, int)]))]).astype(np.int32)
+        P, Hq, Hk, D = 16, 32, 8, 128
+    npg = -(-kv // P)
+    last = (kv - (npg - 1) * P).astype(np.int32)
+    kv_indptr = np.concatenate([[0], np.cumsum(npg)]).astype(np.int32)
+    for wd, wp in ((1, 1), (64, 32), (128, 64), (256, 128)):
+        _compare(qo, kv_indptr, last, page_size=P, num_qo_heads=Hq, num_kv_heads=Hk, head_dim=D,
+                 causal=True, workers_decode=wd, workers_prefill=wp)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(page_size=0), fi.binding.FI_ERR_INVALID_ARG),
+    (dict(num_qo_heads=6, num_kv_heads=4), fi.binding.FI_ERR_INVALID_ARG),
+    (dict(head_dim=96), fi.binding.FI_ERR_UNSUPPORTED),
+    (dict(num_qo_heads=48, num_kv_heads=3), fi.binding.FI_ERR_UNSUPPORTED),
+    (dict(workers_decode=0), fi.binding.FI_ERR_INVALID_ARG),
+    (dict(min_seg_pages=0), fi.binding.FI_ERR_INVALID_ARG),
+    (dict(br_override=24), fi.binding.FI_ERR_INVALID_ARG),
+    (dict(kv_last_page_len=[0, 3]), fi.binding.FI_ERR_INVALID_ARG),
+    (dict(kv_last_page_len=[5, 3]), fi.binding.FI_ERR_INVALID_ARG),
+    (dict(kv_indptr=[1, 2, 3]), fi.binding.FI_ERR_INVALID_ARG),
+    (dict(kv_indptr=[0, 2, 1]), fi.binding.FI_ERR_INVALID_ARG),
+    (dict(qo_indptr=[0, 9, 10]), fi.binding.FI_ERR_INVALID_ARG),
+    (dict(qo_indptr=[0, 2, 1]), fi.binding.FI_ERR_INVALID_ARG),
+])
+def test_fi_plan_error_codes_match_oracle(bad, code):
+    kw = dict(qo_indptr=[0, 2, 3], kv_indptr=[0, 2, 3], kv_last_page_len=[4, 3], page_size=4,
+              num_qo_heads=8, num_kv_heads=2, head_dim=64, causal=True, workers_decode=2,
+              workers_prefill=2)
+    kw.update(bad)
+    args = (kw.pop("qo_indptr"), kw.pop("kv_indptr"), kw.pop("kv_last_page_len"))
+    ocode, _ = pr.plan(*args, **kw)
+    assert ocode == code
+    with pytest.raises(fi.FIError) as e:
+        fi.fi_plan(*args, **kw)
+    assert e.value.code == code
+    assert fi.fi_last_error()
+
+
+def test_fi_plan_capacity_and_bounds():
+    kv_indptr = [0, 3, 10]
+    last = [5, 16]
+    with pytest.raises(fi.FIError) as e:
+        fi.fi_plan(None, kv_indptr, last, page_size=16, num_qo_heads=8, num_kv_heads=2,
+                   head_dim=128, causal=True, workers_decode=4, capacity=10)
+    assert e.value.code == fi.binding.FI_ERR_WORKSPACE_TOO_SMALL
+    rng = np.random.default_rng(5)
+    for _ in range(30):
+        B = int(rng.integers(1, 12))
+        qo = rng.integers(0, 300, B)
+        kv = qo + rng.integers(0, 500, B)
+        npg = -(-kv // 16)
+        lastp = np.where(npg > 0, kv - (npg - 1) * 16, 0)
+        kvi = np.concatenate([[0], np.cumsum(npg)])
+        qoi = np.concatenate([[0], np.cumsum(qo)])
+        wd, wp = int(rng.integers(1, 50)), int(rng.integers(1, 50))
+        ints, ws = fi.fi_plan_bounds(B, int(qoi[-1]), 32, 8, 128, wd, wp)
+        p = fi.fi_plan(qoi, kvi, lastp, page_size=16, num_qo_heads=32, num_kv_heads=8,
+                       head_dim=128, causal=True, workers_decode=wd, workers_prefill=wp,
+                       min_seg_pages=1, br_override=16)
+        assert p.ints <= ints and p.float_ws_bytes <= ws
+
+
+def test_run_calls_reject_bad_arguments_without_a_gpu():
+    """Argument and plan checks happen on the host before any launch."""
+    plan = fi.fi_plan(None, [0, 2], [3], page_size=16, num_qo_heads=8, num_kv_heads=2,
+                      head_dim=128, causal=True, workers_decode=2)
+    L = fi.lib()
+    params = fi.make_params(__import__("torch").bfloat16, __import__("torch").bfloat16, 8, 2, 64, 16)
+    rc = L.fi_batch_decode_paged(plan.host_ptr(), 16, ctypes.byref(params), 16, 16, 10, 16, 16, 16,
+                                 16, None, 16, 1 << 20, None)
+    assert rc == fi.binding.FI_ERR_PLAN_MISMATCH  # plan built for head_dim 128
+    params = fi.make_params(__import__("torch").bfloat16, __import__("torch").bfloat16, 8, 2, 128, 16)
+    rc = L.fi_batch_decode_paged(plan.host_ptr(), 16, ctypes.byref(params), 16, 16, 10, 16, 16, 16,
+                                 16, None, 16, 0, None)
+    assert rc == fi.binding.FI_ERR_WORKSPACE_TOO_SMALL  # checked before any launch
+    bad = np.zeros(64, np.int32)
+    rc = L.fi_batch_decode_paged(bad.ctypes.data, 16, ctypes.byref(params), 16, 16, 10, 16, 16, 16,
+                                 16, None, 16, 1 << 20, None)
+    assert rc == fi.binding.FI_ERR_PLAN_MISMATCH
