@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 
 METRIC = "paged decode HBM GB/s & causal prefill TFLOP/s (bf16), % of MI355X peak"
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6
 NUM_CUS = 256
 
 
@@ -142,6 +143,190 @@ def run_decode_bench(args):
     return result, b, nbytes
 
 
+def prefill_flops(b) -> int:
+    """Causal-visible flops: 4 D per (query head, visible key) pair (QK^T and PV)."""
+    tot = 0
+    for qo, kv in zip(b.qo_lens.tolist(), b.kv_lens.tolist()):
+        if b.causal:
+            tot += qo * (kv - qo) + qo * (qo + 1) // 2
+        else:
+            tot += qo * kv
+    return 4 * b.head_dim * b.num_qo_heads * tot
+
+
+def prefill_slice(b):
+    """The batch restricted to its multi-query requests (same pool and values)."""
+    import workloads as wl
+    keep = [i for i, q in enumerate(b.qo_lens.tolist()) if q >= 2]
+    qo = b.qo_lens[keep]
+    kv_indptr = [0]
+    idx = []
+    qrows = []
+    for i in keep:
+        pages = b.kv_indices[b.kv_indptr[i]:b.kv_indptr[i + 1]]
+        idx.append(pages)
+        kv_indptr.append(kv_indptr[-1] + len(pages))
+        qrows.append(b.q[b.qo_indptr[i]:b.qo_indptr[i + 1]])
+    qo_indptr = np.concatenate([[0], np.cumsum(qo)]).astype(np.int32)
+    import torch
+    return wl.PagedBatch(page_size=b.page_size, num_qo_heads=b.num_qo_heads,
+                         num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, dtype=b.dtype,
+                         causal=b.causal, sm_scale=b.sm_scale, soft_cap=b.soft_cap, qo_lens=qo,
+                         kv_lens=b.kv_lens[keep], qo_indptr=qo_indptr,
+                         kv_indptr=np.asarray(kv_indptr, np.int32),
+                         kv_indices=np.concatenate(idx).astype(np.int32),
+                         kv_last_page_len=b.kv_last_page_len[keep].copy(),
+                         q=torch.cat(qrows), kv_pool=b.kv_pool, name=b.name + "/prefill_slice")
+
+
+def time_batch_call(b, steps, warmup, workers_decode=0, workers_prefill=0, pool_copies=2):
+    """Plan once, then time the run call (decode/prefill kernels + merges) with
+    HIP events on its stream.  Returns (mean ms, plan)."""
+    import torch
+
+    import paged_kv_block_bsr_amd as fi
+    dev = torch.device("cuda", 0)
+    Hk = b.num_kv_heads
+    wd = workers_decode or fi.fi_default_workers(fi.FI_KIND_DECODE, NUM_CUS, Hk)
+    wp = workers_prefill or fi.fi_default_workers(fi.FI_KIND_PREFILL, NUM_CUS, Hk)
+    plan = fi.fi_plan(b.qo_indptr, b.kv_indptr, b.kv_last_page_len, page_size=b.page_size,
+                      num_qo_heads=b.num_qo_heads, num_kv_heads=Hk, head_dim=b.head_dim,
+                      causal=b.causal, workers_decode=wd, workers_prefill=wp)
+    plan_dev = plan.to_device(dev)
+    i32 = lambda a: torch.from_numpy(np.asarray(a, np.int32)).to(dev)
+    pools = [b.kv_pool.to(dev) for _ in range(max(1, pool_copies))]
+    q = b.q.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    ws = torch.empty(plan.float_ws_bytes // 4 + 64, dtype=torch.float32, device=dev)
+    params = fi.make_params(b.dtype, b.dtype, b.num_qo_heads, Hk, b.head_dim, b.page_size,
+                            b.sm_scale, b.soft_cap)
+    qo_d, kvp_d, kvi_d, last_d = (None if b.qo_indptr is None else i32(b.qo_indptr),
+                                  i32(b.kv_indptr), i32(b.kv_indices), i32(b.kv_last_page_len))
+
+    def call(k):
+        if b.qo_indptr is None:
+            fi.fi_batch_decode_paged(plan, plan_dev, params, q, pools[k % len(pools)], kvp_d,
+                                     kvi_d, last_d, o, lse, ws)
+        else:
+            fi.fi_batch_prefill_paged(plan, plan_dev, params, q, pools[k % len(pools)], qo_d,
+                                      kvp_d, kvi_d, last_d, o, lse, ws)
+
+    for k in range(warmup):
+        call(k)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for k in range(steps):
+        ev[k][0].record()
+        call(k)
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+    del pools
+    return ms, plan
+
+
+def secondary_measurements(args):
+    """Prefill slice TFLOP/s, whole mixed step and cascade vs flat (context for
+    the headline decode figure; same kernels, other workloads)."""
+    import workloads as wl
+    out = {}
+    b = wl.mixed_ragged_step()
+    ps = prefill_slice(b)
+    ms, plan = time_batch_call(ps, args.side_steps, 3)
+    fl = prefill_flops(ps)
+    out["prefill_slice"] = {
+        "workload": "mixed_ragged_step prefill requests (16 causal prefills)",
+        "tflops": round(fl / (ms * 1e-3) / 1e12, 2), "peak_tflops": BF16_PEAK_TFLOPS,
+        "frac": round(fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4), "ms": round(ms, 4),
+        "flops": fl, "tile_rows": int(plan.info.prefill_tile_rows),
+        "prefill_items": int(plan.info.prefill_items)}
+    ms, plan = time_batch_call(b, args.side_steps, 3)
+    nb = decode_bytes(b)
+    fl = prefill_flops(b)
+    out["mixed_step"] = {
+        "workload": "mixed_ragged_step (16 prefills + 48 decodes, one call)",
+        "ms": round(ms, 4), "gbs": round(nb / (ms * 1e-3) / 1e9, 1),
+        "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+        "roofline_frac": round(max(nb / (HBM_PEAK_GBS * 1e9), fl / (BF16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3), 4)}
+    del b, ps
+    cb = wl.shared_prefix_cascade()
+    ms_flat, _ = time_batch_call(cb.flat, args.side_steps, 3)
+    ms_casc = time_cascade(cb, args.side_steps, 3)
+    out["cascade"] = {"workload": "shared_prefix_cascade (64 requests, 2048-token prefix, soft-cap 30)",
+                      "cascade_us": round(ms_casc * 1e3, 2), "flat_us": round(ms_flat * 1e3, 2),
+                      "speedup": round(ms_flat / ms_casc, 3)}
+    return out
+
+
+def time_cascade(cb, steps, warmup):
+    import torch
+
+    import paged_kv_block_bsr_amd as fi
+    dev = torch.device("cuda", 0)
+    l0, l1 = cb.level0, cb.level1
+    Hk = l0.num_kv_heads
+    kw = dict(page_size=l0.page_size, num_qo_heads=l0.num_qo_heads, num_kv_heads=Hk,
+              head_dim=l0.head_dim, workers_decode=fi.fi_default_workers(fi.FI_KIND_DECODE, NUM_CUS, Hk),
+              workers_prefill=fi.fi_default_workers(fi.FI_KIND_PREFILL, NUM_CUS, Hk))
+    p0 = fi.fi_plan(l0.qo_indptr, l0.kv_indptr, l0.kv_last_page_len, causal=False, **kw)
+    p1 = fi.fi_plan(None, l1.kv_indptr, l1.kv_last_page_len, causal=True, **kw)
+    i32 = lambda a: torch.from_numpy(np.asarray(a, np.int32)).to(dev)
+    q, pool = l0.q.to(dev), l0.kv_pool.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    ws = torch.empty(fi.fi_cascade_workspace_bytes(p0, p1) // 4 + 64, dtype=torch.float32, device=dev)
+    params = fi.make_params(l0.dtype, l0.dtype, l0.num_qo_heads, Hk, l0.head_dim, l0.page_size,
+                            l0.sm_scale, l0.soft_cap)
+    a0 = (p0, p0.to_device(dev), i32(l0.qo_indptr), i32(l0.kv_indptr), i32(l0.kv_indices),
+          i32(l0.kv_last_page_len))
+    a1 = (p1, p1.to_device(dev), None, i32(l1.kv_indptr), i32(l1.kv_indices),
+          i32(l1.kv_last_page_len))
+
+    def call():
+        fi.fi_cascade(*a0, *a1, params, q, pool, o, lse, ws)
+
+    for _ in range(warmup):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for k in range(steps):
+        ev[k][0].record()
+        call()
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    return float(np.mean([s.elapsed_time(e) for s, e in ev]))
+
+
+def calibrate(reps=10):
+    """Plain torch copy (1 GiB read + 1 GiB written) and a streaming sum over
+    2 GiB: the achievable-bandwidth context and the known-size kernels that
+    scale the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    dev = torch.device("cuda", 0)
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    big = torch.ones(n // 2, dtype=torch.float32, device=dev)  # 2 GiB
+    out = {}
+    for name, fn, moved in (("copy_1GiB", lambda: dst.copy_(src), 2 * n),
+                            ("sum_2GiB", lambda: big.sum(), 2 * n)):
+        for _ in range(3):
+            fn()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s0.record()
+        for _ in range(reps):
+            fn()
+        s1.record()
+        torch.cuda.synchronize()
+        ms = s0.elapsed_time(s1) / reps
+        out[name] = {"us": round(ms * 1e3, 2), "gbs": round(moved / (ms * 1e-3) / 1e9, 1)}
+    return out
+
+
 def cpu_baseline(b, nbytes, budget_s=12.0):
     """The fp64 oracle on the host cores over the whole batch (the sample)."""
     from oracle import attn as ref
@@ -176,13 +361,27 @@ def main():
     ap.add_argument("--min-seg-pages", type=int, default=8)
     ap.add_argument("--pool-copies", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the prefill / mixed / cascade side measurements")
+    ap.add_argument("--side-steps", type=int, default=20)
+    ap.add_argument("--mode", default="bench", choices=["bench", "secondary", "calibrate"],
+                    help="secondary: only the prefill / mixed / cascade measurements; "
+                         "calibrate: only the plain copy / streaming-sum kernels")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
+    if args.mode == "secondary":
+        print(json.dumps(secondary_measurements(args)), flush=True)
+        return
+    if args.mode == "calibrate":
+        print(json.dumps(calibrate()), flush=True)
+        return
     result, b, nbytes = run_decode_bench(args)
+    if not args.no_secondary:
+        result["secondary"] = secondary_measurements(args)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(b, nbytes)
     else:

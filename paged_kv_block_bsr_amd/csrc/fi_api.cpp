@@ -102,8 +102,8 @@ RunArgs base_args(const int32_t* plan_dev, const fi_attn_params* p, const void* 
 // Decode stream, prefill stream (if asked), then the merges of both.
 int run_plan(RunArgs a, const int32_t* ph, bool with_prefill) {
   int rc;
-  if (with_prefill && ph[H_STREAM1 + S_NROWS] != 0)
-    return set_error(FI_ERR_UNSUPPORTED, "prefill tiles are not supported yet");
+  if (with_prefill && ph[H_STREAM1 + S_NROWS] != 0 && a.dtype != FI_BF16)
+    return set_error(FI_ERR_UNSUPPORTED, "prefill tiles need bf16 q / kv");
   a.stream_at = H_STREAM0;
   a.workers = ph[H_STREAM0 + S_W];
   a.max_tasks = a.workers - 1;
@@ -113,7 +113,8 @@ int run_plan(RunArgs a, const int32_t* ph, bool with_prefill) {
     b.stream_at = H_STREAM1;
     b.workers = ph[H_STREAM1 + S_W];
     b.max_tasks = b.workers - 1;
-    if ((rc = launch_prefill(b))) return rc;
+    // fp32 batches hold no prefill tiles (checked above): their prefill kernel is not built
+    if (a.dtype == FI_BF16 && (rc = launch_prefill(b))) return rc;
     if ((rc = launch_merge_partials(a))) return rc;
     return launch_merge_partials(b);
   }

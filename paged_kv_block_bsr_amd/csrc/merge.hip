@@ -29,6 +29,13 @@ struct MergeParams {
   int32_t out_bf16;
 };
 
+constexpr int kMergeRows = 16;  // packed rows per merge block (grid z covers a 128-row tile)
+
+// Block (task, g, z) merges rows 16 z .. 16 z + 15 of split row `task`:
+//  1. per row, 16 threads reduce the slots' lse to the max M and 1 / L;
+//  2. threads take (row, 4-dim chunk) units; when there are fewer units than
+//     threads, the slots are also divided among thread groups and the group
+//     sums are added through LDS, so long slot lists are read in parallel.
 __global__ __launch_bounds__(kThreads) void merge_partials_kernel(MergeParams a) {
   const int32_t* sd = a.plan + a.stream_at;
   const int task = blockIdx.x;
@@ -40,6 +47,9 @@ __global__ __launch_bounds__(kThreads) void merge_partials_kernel(MergeParams a)
   const int req = rows[4 * row + 0];
   const int rb = rows[4 * row + 1];
   const int re = rows[4 * row + 2];
+  const int r0 = kMergeRows * blockIdx.z;
+  if (r0 >= re - rb) return;
+  const int nr = min(kMergeRows, re - rb - r0);
   const int s0 = merge[row], s1 = merge[row + 1];
   // partial layout [slot][Hk][stride][D]; stride = G for decode rows, 128 for tiles
   const int stride = sd[S_KIND] == 0 ? a.G : kMaxTileRows;
@@ -47,30 +57,83 @@ __global__ __launch_bounds__(kThreads) void merge_partials_kernel(MergeParams a)
   const float* wl = a.ws + sd[S_WS_LSE];
   const int qbase = a.qo_indptr ? a.qo_indptr[req] : req;
   const int D = a.D, G = a.G;
-  const int n = (re - rb) * D;
-  for (int idx = threadIdx.x; idx < n; idx += kThreads) {
-    const int r = idx / D, d = idx % D;
-    const int packed = rb + r;
+  const int tid = threadIdx.x;
+  auto lse_at = [&](int s, int r) { return wl[((int64_t)s * a.Hk + g) * stride + r]; };
+
+  __shared__ float sM[kMergeRows], sInv[kMergeRows];
+  __shared__ f32x4_t red[kThreads];
+  {
+    const int rr = tid >> 4, l16 = tid & 15;
     float M = neg_inf();
-    for (int s = s0; s < s1; ++s) M = fmaxf(M, wl[((int64_t)s * a.Hk + g) * stride + r]);
-    float out = 0.f, lse = neg_inf();
-    if (M != neg_inf()) {
-      float L = 0.f, O = 0.f;
-      for (int s = s0; s < s1; ++s) {
-        const int64_t pr = ((int64_t)s * a.Hk + g) * stride + r;
-        const float w = __expf(wl[pr] - M);
-        L += w;
-        O += w * wo[pr * D + d];
-      }
-      out = O / L;
-      lse = M + __logf(L);
+    if (rr < nr)
+      for (int s = s0 + l16; s < s1; s += 16) M = fmaxf(M, lse_at(s, r0 + rr));
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 16));
+    float L = 0.f;
+    if (rr < nr && M != neg_inf())
+      for (int s = s0 + l16; s < s1; s += 16) L += __expf(lse_at(s, r0 + rr) - M);
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) L += __shfl_xor(L, off, 16);
+    if (rr < nr && l16 == 0) {
+      sM[rr] = M;
+      sInv[rr] = M == neg_inf() ? 0.f : 1.f / L;
     }
+  }
+  __syncthreads();
+  const int chunks = D / 4;
+  const int U = nr * chunks;  // (row, 4-dim chunk) units
+  int UP = 1;
+  while (UP < U) UP <<= 1;
+  const int ngroups = UP >= kThreads ? 1 : kThreads / UP;
+  const int sg = UP >= kThreads ? 0 : tid / UP;
+  for (int u = (UP >= kThreads ? tid : tid % UP); u < U; u += (UP >= kThreads ? kThreads : UP)) {
+    const int rr = u / chunks, c = u % chunks;
+    const float M = sM[rr], inv = sInv[rr];
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    if (M != neg_inf()) {
+#pragma unroll 4
+      for (int s = s0 + sg; s < s1; s += ngroups) {
+        const int64_t pr = ((int64_t)s * a.Hk + g) * stride + r0 + rr;
+        const float w = __expf(wl[pr] - M) * inv;
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(wo + pr * D + 4 * c);
+        acc += w * v;
+      }
+    }
+    if (ngroups > 1) {
+      red[tid] = acc;
+      break;  // one unit per thread when the slots are split among groups
+    }
+    const int packed = rb + r0 + rr;
     const int64_t orow = (int64_t)(qbase + packed / G) * a.Hq + g * G + packed % G;
-    if (a.out_bf16)
-      reinterpret_cast<uint16_t*>(a.o)[orow * D + d] = (uint16_t)f32_to_bf16_bits(out);
-    else
-      reinterpret_cast<float*>(a.o)[orow * D + d] = out;
-    if (a.lse && d == 0) a.lse[orow] = lse;
+    if (a.out_bf16) {
+      uint32_t lo = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
+      uint32_t hi = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
+      reinterpret_cast<uint32_t*>(a.o)[(orow * D + 4 * c) / 2] = lo;
+      reinterpret_cast<uint32_t*>(a.o)[(orow * D + 4 * c) / 2 + 1] = hi;
+    } else {
+      *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.o) + orow * D + 4 * c) = acc;
+    }
+    if (a.lse && c == 0) a.lse[orow] = M == neg_inf() ? neg_inf() : M + __logf(1.f / inv);
+  }
+  if (ngroups > 1) {
+    __syncthreads();
+    if (tid < U) {
+      f32x4_t acc = red[tid];
+      for (int k = 1; k < ngroups; ++k) acc += red[tid + k * UP];
+      const int rr = tid / chunks, c = tid % chunks;
+      const float M = sM[rr], inv = sInv[rr];
+      const int packed = rb + r0 + rr;
+      const int64_t orow = (int64_t)(qbase + packed / G) * a.Hq + g * G + packed % G;
+      if (a.out_bf16) {
+        uint32_t lo = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
+        uint32_t hi = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
+        reinterpret_cast<uint32_t*>(a.o)[(orow * D + 4 * c) / 2] = lo;
+        reinterpret_cast<uint32_t*>(a.o)[(orow * D + 4 * c) / 2 + 1] = hi;
+      } else {
+        *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.o) + orow * D + 4 * c) = acc;
+      }
+      if (a.lse && c == 0) a.lse[orow] = M == neg_inf() ? neg_inf() : M + __logf(1.f / inv);
+    }
   }
 }
 
@@ -127,7 +190,9 @@ int launch_merge_partials(const RunArgs& r) {
   p.G = r.G;
   p.stream_at = r.stream_at;
   p.out_bf16 = r.out_dtype == FI_BF16;
-  dim3 grid(std::max(1, r.max_tasks), r.Hk), block(kThreads);
+  // decode rows hold G <= 8 packed rows; prefill tiles up to 128 (8 blocks of 16)
+  const int z = r.stream_at == H_STREAM0 ? 1 : kMaxTileRows / kMergeRows;
+  dim3 grid(std::max(1, r.max_tasks), r.Hk, z), block(kThreads);
   hipLaunchKernelGGL(merge_partials_kernel, grid, block, 0, (hipStream_t)r.hip_stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(FI_ERR_HIP, "merge launch: %s", hipGetErrorString(e));

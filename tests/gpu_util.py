@@ -95,3 +95,31 @@ def assert_close(o, lse, o_ref, lse_ref, what="", atol=ATOL, rtol=RTOL, lse_atol
         if empty.any():
             assert np.all(o[empty] == 0.0), f"{what}: empty rows must have o = 0"
     return float(err.max()) if err.size else 0.0
+
+
+def run_cascade(cb, workers_decode=None, workers_prefill=None, min_seg_pages=8, out_dtype=None):
+    """fi_cascade over a CascadeBatch: level 0 (groups over the shared pages,
+    non-causal) merged with level 1 (each request's own pages)."""
+    l0, l1 = cb.level0, cb.level1
+    Hk = l0.num_kv_heads
+    wd = workers_decode or fi.fi_default_workers(fi.FI_KIND_DECODE, NUM_CUS, Hk)
+    wp = workers_prefill or fi.fi_default_workers(fi.FI_KIND_PREFILL, NUM_CUS, Hk)
+    kw = dict(page_size=l0.page_size, num_qo_heads=l0.num_qo_heads, num_kv_heads=Hk,
+              head_dim=l0.head_dim, workers_decode=wd, workers_prefill=wp,
+              min_seg_pages=min_seg_pages)
+    plan0 = fi.fi_plan(l0.qo_indptr, l0.kv_indptr, l0.kv_last_page_len, causal=False, **kw)
+    plan1 = fi.fi_plan(l1.qo_indptr, l1.kv_indptr, l1.kv_last_page_len, causal=l1.causal, **kw)
+    d0, d1 = DeviceBatch(l0), DeviceBatch(l1)
+    d1.q, d1.pool = d0.q, d0.pool  # one query tensor and one pool: only the index arrays differ
+    out_dtype = out_dtype or l0.dtype
+    o = torch.full(tuple(l0.q.shape), float("nan"), dtype=out_dtype, device="cuda")
+    lse = torch.full(tuple(l0.q.shape[:2]), float("nan"), dtype=torch.float32, device="cuda")
+    nbytes = fi.fi_cascade_workspace_bytes(plan0, plan1)
+    ws = torch.empty(nbytes // 4 + 64, dtype=torch.float32, device="cuda")
+    params = fi.make_params(l0.dtype, out_dtype, l0.num_qo_heads, Hk, l0.head_dim, l0.page_size,
+                            l0.sm_scale, l0.soft_cap)
+    fi.fi_cascade(plan0, plan0.to_device(), d0.qo_indptr, d0.kv_indptr, d0.kv_indices, d0.last,
+                  plan1, plan1.to_device(), d1.qo_indptr, d1.kv_indptr, d1.kv_indices, d1.last,
+                  params, d0.q, d0.pool, o, lse, ws)
+    torch.cuda.synchronize()
+    return o.float().cpu(), lse.cpu()

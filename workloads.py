@@ -260,13 +260,15 @@ def shared_prefix_cascade(nan_poison=False, num_requests=64, prefix_len=2048,
         f_idx.append(np.concatenate([prefix_ids, own]))
         f_indptr[i + 1] = f_indptr[i] + n_prefix + len(own)
     f_indices = np.concatenate(f_idx).astype(np.int32)
+    # an empty suffix leaves the (full) last prefix page as the flat view's last page
+    f_last = np.where(suffix > 0, s_last, P).astype(np.int32)
     if nan_poison:
-        _poison(pool, f_indptr, f_indices, s_last, P)
+        _poison(pool, f_indptr, f_indices, f_last, P)
     common = dict(page_size=P, num_qo_heads=Hq, num_kv_heads=Hk, head_dim=D, dtype=dtype,
                   sm_scale=1.0 / math.sqrt(D), soft_cap=float(soft_cap), q=q, kv_pool=pool)
     ones = np.ones(num_requests, np.int64)
     flat = PagedBatch(causal=True, qo_lens=ones, kv_lens=prefix_len + suffix, qo_indptr=None,
-                      kv_indptr=f_indptr, kv_indices=f_indices, kv_last_page_len=s_last.copy(),
+                      kv_indptr=f_indptr, kv_indices=f_indices, kv_last_page_len=f_last,
                       name="shared_prefix_cascade/flat", **common)
     level0 = PagedBatch(causal=False, qo_lens=np.array([num_requests], np.int64),
                         kv_lens=np.array([prefix_len], np.int64),
