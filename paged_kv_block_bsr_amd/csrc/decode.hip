@@ -32,6 +32,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kChunk = 16;
+constexpr float kMaxSlack = 8.f;  // log2-domain headroom of the lazily updated running max
 
 struct DecodeParams {
   const int32_t* plan;
@@ -62,6 +63,8 @@ struct Shape {
   static constexpr int NK = D / (4 * E);    // K loads per lane per chunk
   static_assert(NL == NK, "K and V loads per chunk differ");
 };
+
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 
 template <typename T, int NK>
 __device__ __forceinline__ f32x4_t qk_mfma(const u32x4_t (&kp)[NK], const u32x4_t (&qp)[NK]) {
@@ -164,12 +167,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams a) {
       int pg = a.kv_indices[kvb + (FAST ? (tok >> a.page_shift) : tok / P)];
       return (uint32_t)pg < (uint64_t)a.pool_pages ? (int64_t)pg : 0;  // never read outside the pool
     };
+    // Page ids of this wave's chunks, 64 at a time: lane j holds the page of
+    // the wave's chunk 64 * batch + j, read back with readlane when its loads
+    // are issued, so no page lookup sits in front of the K/V loads.
+    int pid_vec = 0;
+    auto load_pids = [&](int batch) {
+      const int c = wave + kWaves * (64 * batch + lane);
+      pid_vec = c < nch ? (int)page_of(t0 + c * kChunk) : 0;
+    };
 
-    // Issue the K and V loads of chunk c.
-    auto load_chunk = [&](int c, u32x4_t (&kb)[NK], u32x4_t (&vb)[NL]) {
+    // Issue the K and V loads of chunk c (the wave's kth-th chunk).
+    auto load_chunk = [&](int c, int kth, u32x4_t (&kb)[NK], u32x4_t (&vb)[NL]) {
       const int cs = t0 + c * kChunk;
       if constexpr (FAST) {
-        const int64_t page = page_of(cs);
+        if ((kth & 63) == 0) load_pids(kth >> 6);
+        const int64_t page = __builtin_amdgcn_readlane(pid_vec, kth & 63);
         const int slot0 = cs & (P - 1);
         const uint8_t* pbase = a.kv + (page * page_stride + (int64_t)g * D) * TB;
         const int tkk = min(cs + tk, t1 - 1) - cs;
@@ -212,7 +224,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams a) {
       float cm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       cm = fmaxf(cm, __shfl_xor(cm, 16));
       cm = fmaxf(cm, __shfl_xor(cm, 32));
-      const float m_new = fmaxf(m_run, cm);
+      // The reference max only moves when the chunk beats it by more than
+      // 2^8: weights stay <= 256 (safe in fp32) and most chunks need no rescale.
+      const float m_new = cm > m_run + kMaxSlack ? cm : m_run;
       const float m_use = m_new == neg_inf() ? 0.f : m_new;
       const float alpha = fast_exp2(m_run - m_use);
       float p[4];
@@ -238,34 +252,50 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams a) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      bool rescale = false;
 #pragma unroll
-      for (int h = 0; h < G; ++h)
+      for (int h = 0; h < G; ++h) rescale |= al[h] != 1.f;
+      if (rescale) {  // wave-uniform: al[] is the same LDS value in every lane
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[h][e] *= al[h];
+        for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int k = 0; k < NL; ++k) {
-        // a V token past t1 was loaded from a clamped address; give it zero weight
-        const bool valid = cs + vr * NL + k < t1;
+          for (int e = 0; e < E; ++e) acc[h][e] *= al[h];
+      }
+      if (cs + kChunk <= t1) {  // whole chunk valid (wave-uniform)
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const float v = valid ? piece_elem<T>(vb[k], e) : 0.f;
+        for (int k = 0; k < NL; ++k)
 #pragma unroll
-          for (int h = 0; h < G; ++h) acc[h][e] = fmaf(pv[h][k], v, acc[h][e]);
+          for (int e = 0; e < E; ++e) {
+            const float v = piece_elem<T>(vb[k], e);
+#pragma unroll
+            for (int h = 0; h < G; ++h) acc[h][e] = fmaf(pv[h][k], v, acc[h][e]);
+          }
+      } else {
+#pragma unroll
+        for (int k = 0; k < NL; ++k) {
+          // a V token past t1 was loaded from a clamped address; give it zero weight
+          const bool valid = cs + vr * NL + k < t1;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const float v = valid ? piece_elem<T>(vb[k], e) : 0.f;
+#pragma unroll
+            for (int h = 0; h < G; ++h) acc[h][e] = fmaf(pv[h][k], v, acc[h][e]);
+          }
         }
       }
     };
 
-    // chunks of this wave: wave, wave + 4, ...; two register sets in flight
+    // chunks of this wave: wave + 4 k, k = 0, 1, ...; two register sets in flight
     {
       u32x4_t kA[NK], vA[NL], kB[NK], vB[NL];
-      int c = wave;
-      if (c < nch) load_chunk(c, kA, vA);
-      for (; c < nch; c += 2 * kWaves) {
-        if (c + kWaves < nch) load_chunk(c + kWaves, kB, vB);
-        compute_chunk(c, kA, vA);
-        if (c + kWaves >= nch) break;
-        if (c + 2 * kWaves < nch) load_chunk(c + 2 * kWaves, kA, vA);
-        compute_chunk(c + kWaves, kB, vB);
+      const int myn = nch > wave ? (nch - wave + kWaves - 1) / kWaves : 0;
+      if (myn > 0) load_chunk(wave, 0, kA, vA);
+      for (int k = 0; k < myn; k += 2) {
+        if (k + 1 < myn) load_chunk(wave + kWaves * (k + 1), k + 1, kB, vB);
+        compute_chunk(wave + kWaves * k, kA, vA);
+        if (k + 1 >= myn) break;
+        if (k + 2 < myn) load_chunk(wave + kWaves * (k + 2), k + 2, kA, vA);
+        compute_chunk(wave + kWaves * (k + 1), kB, vB);
       }
     }
 
@@ -321,6 +351,260 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 decode with page_size a power of two >= 16: P.V on the matrix cores.
+//
+// Per wave and 16-token chunk: K goes global -> VGPRs as the A operand of
+// S = K Q^T (v_mfma_f32_16x16x32_bf16, as above); V goes global -> LDS by
+// direct-to-LDS loads (no VGPRs held while in flight) into a two-stage ring
+// private to the wave, row-major with the 16-byte pieces of token t stored at
+// piece ^ (t mod pieces-per-row) to spread LDS banks; ds_read_b64_tr_b16 then
+// returns, per lane, 4 consecutive tokens of one dim, which is the V^T A
+// operand of v_mfma_f32_16x16x16_bf16; its B operand (tokens 4 (l/16) .. +3
+// of head l % 16) is exactly how the S accumulator holds P, so P never leaves
+// the lane.  P is split into bf16 hi + lo parts (two MFMAs), keeping ~16 bits.
+// O^T accumulates in 4 registers per 16-dim block; lane l owns head l % 16.
+// The compiler does not track direct-to-LDS loads, so the kernel waits on
+// vmcnt itself before reading a stage.
+// ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+#define FI_LDS __attribute__((address_space(3)))
+
+// s_waitcnt with vmcnt <= n and no wait on the other counters (gfx9 encoding)
+#define FI_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) { return f32_to_bf16_bits(f); }
+
+template <int D, int G, typename OT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void decode_mfma_kernel(DecodeParams a) {
+  constexpr int RB = D * 2;              // bytes of one K / V row of one head
+  constexpr int NP = RB / 16;            // 16-byte pieces per row
+  constexpr int NK = D / 32;             // K loads per lane per chunk
+  constexpr int NV = kChunk * RB / 1024; // direct-to-LDS V loads per wave per chunk
+  constexpr int NB = D / 16;             // 16-dim output blocks
+  constexpr int kStage = kChunk * RB;    // bytes of one V stage
+  static_assert(NK == NV, "one K and one V load per 32 dims");
+
+  __shared__ __align__(16) uint8_t vring[kWaves][2][kStage];
+  __shared__ float m_lds[kWaves][G];
+  __shared__ float l_lds[kWaves][G];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int worker = blockIdx.x;
+  const int g = blockIdx.y;
+  const int32_t* sd = a.plan + a.stream_at;
+  const int32_t* rows = a.plan + sd[S_OFF_ROWS];
+  const int32_t* items = a.plan + sd[S_OFF_ITEMS];
+  const int32_t* wip = a.plan + sd[S_OFF_WIP];
+  float* ws_o = a.ws + sd[S_WS_O];
+  float* ws_lse = a.ws + sd[S_WS_LSE];
+  const int P = a.P;
+  const int Hk = a.Hk;
+  const int64_t tok_stride = (int64_t)Hk * D;
+  const int64_t half_stride = (int64_t)P * tok_stride;
+  const int64_t page_stride = 2 * half_stride;
+  const int tk = lane & 15;   // S lane: token row of K; head column
+  const int kq = lane >> 4;   // S lane: dim slice of K, token quad of S
+  const int hS = lane & 15;
+  // direct-to-LDS V load k of lane l covers LDS bytes k*1024 + 16 l of the stage
+  // = token (k*1024 + 16 l) / RB, stored piece ((16 l) % RB) / 16
+  // transposed read: source lane (group gq, j) points at token 4 gq + j/4,
+  // dims 16 b + 4 (j % 4) .. + 4
+  const int tr_tok = 4 * kq + (tk >> 2);
+  const int tr_sub = tk & 3;
+
+  float* acc_lds = reinterpret_cast<float*>(&vring[0][0][0]);  // epilogue reuse: [kWaves][G][D]
+  static_assert(sizeof(float) * kWaves * G * D <= sizeof(vring), "epilogue scratch");
+
+  const int it_begin = wip[worker];
+  const int it_end = wip[worker + 1];
+  for (int it = it_begin; it < it_end; ++it) {
+    const int row = items[4 * it + 0];
+    const int pb = items[4 * it + 1];
+    const int pe = items[4 * it + 2];
+    const int slot = items[4 * it + 3];
+    const int req = rows[4 * row + 0];
+    const int kvb = a.kv_indptr[req];
+    const int npg = a.kv_indptr[req + 1] - kvb;
+    const int kv_len = npg ? (npg - 1) * P + a.kv_last[req] : 0;
+    const int t0 = pb * P;
+    const int t1 = min(pe * P, kv_len);
+    const int qrow = a.qo_indptr ? a.qo_indptr[req] : req;
+    const int nch = t1 > t0 ? (t1 - t0 + kChunk - 1) / kChunk : 0;
+
+    u32x4_t qp[NK];
+    {
+      const uint8_t* qb = a.q + ((int64_t)qrow * a.Hq + (int64_t)g * G + (hS < G ? hS : 0)) * RB;
+#pragma unroll
+      for (int p = 0; p < NK; ++p) {
+        qp[p] = load16(qb + (4 * p + kq) * 16);
+        if (hS >= G) qp[p] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+    float m_run = neg_inf();
+    float l_part = 0.f;
+    f32x4_t oacc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) oacc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    int pid_vec = 0;
+    auto load_pids = [&](int batch) {
+      const int c = wave + kWaves * (64 * batch + lane);
+      int pg = c < nch ? a.kv_indices[kvb + ((t0 + c * kChunk) >> a.page_shift)] : 0;
+      pid_vec = (uint32_t)pg < (uint64_t)a.pool_pages ? pg : 0;  // never read outside the pool
+    };
+    // K -> registers, V -> LDS stage `st` for the wave's kth chunk c
+    auto issue = [&](int c, int kth, int st, u32x4_t (&kb)[NK]) {
+      if ((kth & 63) == 0) load_pids(kth >> 6);
+      const int cs = t0 + c * kChunk;
+      const int64_t page = __builtin_amdgcn_readlane(pid_vec, kth & 63);
+      const int slot0 = cs & (P - 1);
+      const int last = t1 - 1 - cs;  // last valid token of the chunk (may exceed 15)
+      const uint8_t* pbase = a.kv + (page * page_stride + (int64_t)g * D) * 2;
+      const uint8_t* kaddr = pbase + (int64_t)(slot0 + min(tk, last)) * tok_stride * 2;
+#pragma unroll
+      for (int p = 0; p < NK; ++p) kb[p] = load16(kaddr + (4 * p + kq) * 16);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int t = (k * 1024 + 16 * lane) / RB;
+        const int pp = ((16 * lane) % RB) / 16;
+        const int piece = pp ^ (t & (NP - 1));
+        const uint8_t* src = pbase + (half_stride + (int64_t)(slot0 + min(t, last)) * tok_stride) * 2 + piece * 16;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                         (FI_LDS void*)(&vring[wave][st][k * 1024]), 16, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    auto compute = [&](int c, int st, const u32x4_t (&kb)[NK]) {
+      const int cs = t0 + c * kChunk;
+      f32x4_t s = qk_mfma<BF16, NK>(kb, qp);
+      float x[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = s[r];
+        if (a.cap > 0.f)
+          v = a.cap * tanh_from_exp(v * a.scale / a.cap) * kLog2e;
+        else
+          v *= a.scale_log2;
+        x[r] = (cs + 4 * kq + r < t1) ? v : neg_inf();
+      }
+      float cm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      cm = fmaxf(cm, __shfl_xor(cm, 16));
+      cm = fmaxf(cm, __shfl_xor(cm, 32));
+      const float m_new = cm > m_run + kMaxSlack ? cm : m_run;
+      const float m_use = m_new == neg_inf() ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      m_run = m_new;
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(x[r] - m_use);
+      l_part = l_part * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+      if (__any(hS < G && alpha != 1.f)) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) oacc[b] *= alpha;
+      }
+      // P^T as bf16 hi + lo parts
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        hi[r] = bf16_bits_rne(p[r]);
+        lo[r] = bf16_bits_rne(p[r] - __uint_as_float(hi[r] << 16));
+      }
+      const s16x4_t bhi = __builtin_bit_cast(s16x4_t, u32x2_t{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)});
+      const s16x4_t blo = __builtin_bit_cast(s16x4_t, u32x2_t{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)});
+      const FI_LDS uint8_t* stage = (const FI_LDS uint8_t*)(&vring[wave][st][0]);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int dim = 16 * b + 4 * tr_sub;
+        const int piece = (dim >> 3) ^ (tr_tok & (NP - 1));
+        FI_LDS s16x4_t* src = (FI_LDS s16x4_t*)(stage + tr_tok * RB + piece * 16 + (dim & 7) * 2);
+        const s16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(src);
+        oacc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, bhi, oacc[b], 0, 0, 0);
+        oacc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, blo, oacc[b], 0, 0, 0);
+      }
+    };
+
+    {
+      u32x4_t kA[NK], kB[NK];
+      const int myn = nch > wave ? (nch - wave + kWaves - 1) / kWaves : 0;
+      if (myn > 0) issue(wave, 0, 0, kA);
+      for (int k = 0; k < myn; k += 2) {
+        const bool n1 = k + 1 < myn;
+        if (n1) issue(wave + kWaves * (k + 1), k + 1, 1, kB);
+        if (n1) FI_WAIT_VMCNT(2 * NK); else FI_WAIT_VMCNT(0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(wave + kWaves * k, 0, kA);
+        __builtin_amdgcn_sched_barrier(0);
+        if (!n1) break;
+        const bool n2 = k + 2 < myn;
+        if (n2) issue(wave + kWaves * (k + 2), k + 2, 0, kA);
+        if (n2) FI_WAIT_VMCNT(2 * NK); else FI_WAIT_VMCNT(0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(wave + kWaves * (k + 1), 1, kB);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // wave totals, then merge the four waves through LDS
+    l_part += __shfl_xor(l_part, 16);
+    l_part += __shfl_xor(l_part, 32);
+    __syncthreads();  // every wave is done with its V ring before it turns into scratch
+    if (lane < G) {
+      m_lds[wave][lane] = m_run;
+      l_lds[wave][lane] = l_part;
+    }
+    if (hS < G) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc_lds[(wave * G + hS) * D + 16 * b + 4 * kq + r] = oacc[b][r];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+      const int h = idx / D, d = idx % D;
+      float M = neg_inf();
+#pragma unroll
+      for (int wv = 0; wv < kWaves; ++wv) M = fmaxf(M, m_lds[wv][h]);
+      float out = 0.f, lse2 = neg_inf();
+      if (M != neg_inf()) {
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < kWaves; ++wv) {
+          const float sc = fast_exp2(m_lds[wv][h] - M);
+          L += l_lds[wv][h] * sc;
+          O += acc_lds[(wv * G + h) * D + d] * sc;
+        }
+        out = O / L;
+        lse2 = M + fast_log2(L);
+      }
+      const int head = g * G + h;
+      if (slot < 0) {
+        store_out<OT>(a.o, ((int64_t)qrow * a.Hq + head) * D + d, out);
+        if (a.lse && d == 0) a.lse[(int64_t)qrow * a.Hq + head] = lse2 * kLn2;
+      } else {
+        const int64_t prow = ((int64_t)slot * Hk + g) * G + h;
+        ws_o[prow * D + d] = out;
+        if (d == 0) ws_lse[prow] = lse2 * kLn2;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int D, int G, typename OT>
+int launch_mfma(const RunArgs& r, const DecodeParams& p) {
+  dim3 grid(r.workers, r.Hk), block(kThreads);
+  hipLaunchKernelGGL((decode_mfma_kernel<D, G, OT>), grid, block, 0, (hipStream_t)r.hip_stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(FI_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return FI_OK;
+}
+
 template <typename T, int D, int G, bool FAST, typename OT>
 int launch_t(const RunArgs& r, const DecodeParams& p) {
   dim3 grid(r.workers, r.Hk), block(kThreads);
@@ -333,6 +617,9 @@ int launch_t(const RunArgs& r, const DecodeParams& p) {
 
 template <typename T, int D, int G, typename OT>
 int launch_fast(const RunArgs& r, const DecodeParams& p) {
+  if constexpr (T::kBytes == 2) {
+    if (p.page_shift >= 0) return launch_mfma<D, G, OT>(r, p);
+  }
   return p.page_shift >= 0 ? launch_t<T, D, G, true, OT>(r, p) : launch_t<T, D, G, false, OT>(r, p);
 }
 

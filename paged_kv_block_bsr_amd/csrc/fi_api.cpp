@@ -99,26 +99,26 @@ RunArgs base_args(const int32_t* plan_dev, const fi_attn_params* p, const void* 
   return a;
 }
 
-// Decode stream, prefill stream (if asked), then the merges of both.
+// Decode stream, prefill stream, then the merges of split rows.  A kernel is
+// launched only when its stream holds rows (merges: split rows), as read from
+// the host copy of the plan; every launch keeps the fixed grid of its stream.
 int run_plan(RunArgs a, const int32_t* ph, bool with_prefill) {
   int rc;
-  if (with_prefill && ph[H_STREAM1 + S_NROWS] != 0 && a.dtype != FI_BF16)
-    return set_error(FI_ERR_UNSUPPORTED, "prefill tiles need bf16 q / kv");
+  const bool dec = ph[H_STREAM0 + S_NROWS] != 0;
+  const bool pre = with_prefill && ph[H_STREAM1 + S_NROWS] != 0;
+  if (pre && a.dtype != FI_BF16) return set_error(FI_ERR_UNSUPPORTED, "prefill tiles need bf16 q / kv");
   a.stream_at = H_STREAM0;
   a.workers = ph[H_STREAM0 + S_W];
   a.max_tasks = a.workers - 1;
-  if ((rc = launch_decode(a))) return rc;
-  if (with_prefill) {
-    RunArgs b = a;
-    b.stream_at = H_STREAM1;
-    b.workers = ph[H_STREAM1 + S_W];
-    b.max_tasks = b.workers - 1;
-    // fp32 batches hold no prefill tiles (checked above): their prefill kernel is not built
-    if (a.dtype == FI_BF16 && (rc = launch_prefill(b))) return rc;
-    if ((rc = launch_merge_partials(a))) return rc;
-    return launch_merge_partials(b);
-  }
-  return launch_merge_partials(a);
+  RunArgs b = a;
+  b.stream_at = H_STREAM1;
+  b.workers = ph[H_STREAM1 + S_W];
+  b.max_tasks = b.workers - 1;
+  if (dec && (rc = launch_decode(a))) return rc;
+  if (pre && (rc = launch_prefill(b))) return rc;
+  if (dec && ph[H_STREAM0 + S_NSPLIT] != 0 && (rc = launch_merge_partials(a))) return rc;
+  if (pre && ph[H_STREAM1 + S_NSPLIT] != 0 && (rc = launch_merge_partials(b))) return rc;
+  return FI_OK;
 }
 
 int check_common(const int32_t* plan_host, const int32_t* plan_dev, const fi_attn_params* params,
@@ -283,8 +283,8 @@ int fi_version(void) { return 100; }
 
 int fi_default_workers(int kind, int num_cus, int num_kv_heads) {
   if (num_cus < 1 || num_kv_heads < 1) return 1;
-  // decode: 4 workgroups of 4 waves per CU; prefill: 2 workgroups per CU
-  const int per_cu = kind == FI_KIND_PREFILL ? 2 : 4;
+  // decode: 3 workgroups of 4 waves per CU (3 waves per SIMD); prefill: 2 per CU
+  const int per_cu = kind == FI_KIND_PREFILL ? 2 : 3;
   int w = per_cu * num_cus / num_kv_heads;
   return w < 1 ? 1 : w;
 }

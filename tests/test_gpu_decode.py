@@ -121,3 +121,15 @@ def test_merge_state_two_way(dt):
     fi.fi_merge_state(dva, dsa, dvb, dsb, dva, dsa)
     torch.cuda.synchronize()
     assert_close(dva.float().cpu(), dsa.cpu(), eo, el, "merge_state in place")
+
+
+def test_long_items_reload_page_ids():
+    """Few workers over a long request: each wave walks more than 64 chunks,
+    so the per-wave page-id vector is reloaded mid-item."""
+    b = wl.make_batch(13, None, [40000, 700, 5], page_size=16, num_qo_heads=32, num_kv_heads=8,
+                      head_dim=128, dtype=torch.bfloat16, decode=True)
+    o_ref, l_ref = ref.attention_of(b)
+    for wd in (1, 2):
+        note(f"long items W={wd}")
+        o, lse, _ = run(b, workers_decode=wd, min_seg_pages=1)
+        assert_close(o, lse, o_ref, l_ref, f"long items W={wd}")
