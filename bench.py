@@ -37,6 +37,27 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_mfma_kernel_llama8b_decode_pmc.json")
+
+
+def counter_traffic(workload):
+    """HBM bytes per decode-kernel dispatch from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, scaled by the copy-kernel calibration;
+    None when that summary was taken on another workload or on a decode
+    kernel source that has changed since."""
+    import hashlib
+    try:
+        d = json.load(open(PMC_SUMMARY))
+        src = open(os.path.join(ROOT, d["source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest()[:16] != d["source_sha256_16"]:
+        return None
+    if workload != "llama8b_decode":
+        return None
+    return int(d["traffic_bytes_per_dispatch"])
+
+
 def decode_bytes(b) -> int:
     """Algorithmic bytes of one decode pass (the method's own traffic)."""
     esz = 2 if b.dtype.itemsize == 2 else 4
@@ -135,7 +156,7 @@ def run_decode_bench(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(nbytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": counter_traffic(args.workload),
             "kernel_ms": round(call_ms, 5),
             "kernel": "decode_kernel + merge_partials_kernel (one fi_batch_decode_paged call)",
         },
