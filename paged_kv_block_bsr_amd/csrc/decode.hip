@@ -52,6 +52,7 @@ struct DecodeParams {
   float scale_log2;    // sm_scale * log2(e)
   float scale;         // sm_scale
   float cap;           // soft-cap; 0 = off
+  float inv_cap;       // 1 / cap (0 when off)
 };
 
 template <typename T, int D>
@@ -212,14 +213,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams a) {
       const int cs = t0 + c * kChunk;
       f32x4_t s = qk_mfma<T, NK>(kb, qp);
       float x[4];
+      if (a.cap > 0.f) {
+        const float c_in = a.scale * a.inv_cap, c_out = a.cap * kLog2e;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = s[r];
-        if (a.cap > 0.f)
-          v = a.cap * tanh_from_exp(v * a.scale / a.cap) * kLog2e;
-        else
-          v *= a.scale_log2;
-        x[r] = (cs + 4 * kq + r < t1) ? v : neg_inf();
+        for (int r = 0; r < 4; ++r) x[r] = c_out * tanh_from_exp(s[r] * c_in);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = s[r] * a.scale_log2;
+      }
+      if (cs + kChunk > t1) {  // tail chunk
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = (cs + 4 * kq + r < t1) ? x[r] : neg_inf();
       }
       float cm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       cm = fmaxf(cm, __shfl_xor(cm, 16));
@@ -484,14 +488,17 @@ void decode_mfma_kernel(DecodeParams a) {
       const int cs = t0 + c * kChunk;
       f32x4_t s = qk_mfma<BF16, NK>(kb, qp);
       float x[4];
+      if (a.cap > 0.f) {
+        const float c_in = a.scale * a.inv_cap, c_out = a.cap * kLog2e;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = s[r];
-        if (a.cap > 0.f)
-          v = a.cap * tanh_from_exp(v * a.scale / a.cap) * kLog2e;
-        else
-          v *= a.scale_log2;
-        x[r] = (cs + 4 * kq + r < t1) ? v : neg_inf();
+        for (int r = 0; r < 4; ++r) x[r] = c_out * tanh_from_exp(s[r] * c_in);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = s[r] * a.scale_log2;
+      }
+      if (cs + kChunk > t1) {  // tail chunk
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = (cs + 4 * kq + r < t1) ? x[r] : neg_inf();
       }
       float cm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       cm = fmaxf(cm, __shfl_xor(cm, 16));
@@ -669,6 +676,7 @@ int launch_decode(const RunArgs& r) {
   p.scale = r.sm_scale;
   p.scale_log2 = r.sm_scale * kLog2e;
   p.cap = r.soft_cap;
+  p.inv_cap = r.soft_cap > 0.f ? 1.f / r.soft_cap : 0.f;
   if (r.dtype == FI_BF16 && r.out_dtype == FI_BF16) return launch_d<BF16, BF16>(r, p);
   if (r.dtype == FI_BF16 && r.out_dtype == FI_F32) return launch_d<BF16, F32>(r, p);
   if (r.dtype == FI_F32 && r.out_dtype == FI_F32) return launch_d<F32, F32>(r, p);

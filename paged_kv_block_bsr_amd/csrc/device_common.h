@@ -37,10 +37,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// tanh from its definition, tanh(y) = 1 - 2 / (e^{2y} + 1); saturates to +-1.
+// tanh from its definition, tanh(y) = 1 - 2 / (e^{2y} + 1), with the
+// hardware reciprocal; saturates to +-1 (e -> inf gives 1, e -> 0 gives -1).
 __device__ __forceinline__ float tanh_from_exp(float y) {
   float e = fast_exp2(2.0f * kLog2e * y);
-  return 1.0f - 2.0f / (e + 1.0f);
+  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
 }
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
