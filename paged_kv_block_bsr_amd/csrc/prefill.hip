@@ -10,41 +10,48 @@
 // workers, whose partial (o, lse) states are merged afterwards (paper page,
 // "Load balancing that survives CUDA graphs").
 //
-// Mapping.  grid = workers x KV heads (1-D, XCD-major), 512 threads = 8
+// Mapping.  grid = workers x KV heads (1-D, XCD-major), 256 threads = 4
 // waves.  A work item is a tile of up to 128 packed rows (packed row r =
 // token r / G, head r % G of the KV head's group) times a range of KV pages.
-// Wave w owns packed rows 16w .. 16w + 15; lane l holds row l % 16 together
-// with the three other lanes l % 16 + 16 k.  Per 64-key KV tile:
-//   - the workgroup gathers K (row-major, padded rows) and V (transposed,
-//     V^T[dim][key] in fp16, keys permuted inside each 32-key group) into
-//     LDS, double buffered, with the next tile's global loads in flight;
-//   - S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = K from LDS, B = the
-//     wave's packed query rows in registers): lane l holds keys
-//     16 m + 4 (l / 16) + r of query l % 16, so the row max and sum need two
-//     cross-lane exchanges;
-//   - online softmax in registers (base-2 exponentials, scale folded in);
-//   - O^T += V^T P^T with v_mfma_f32_16x16x32_f16; P^T comes straight from
-//     the S^T registers because the V^T key order in LDS matches the order in
-//     which the S^T accumulator holds keys.  P (in [0, 1]) and V run in fp16:
-//     bf16 V converts exactly in fp16's normal range (the conversion
-//     saturates at +-65504), and fp16 keeps 11 bits of P where bf16 keeps 8,
-//     which bounds the PV rounding error by 2^-11 max|v| even for rows that
-//     see only a few keys.
+// Wave w owns packed rows 32 w .. 32 w + 31; lane l holds row l % 32, and
+// lanes l and l + 32 split each 32-key block between them.  Per 64-key tile:
+//   - K goes global -> LDS directly (row-major, 16-byte pieces XOR-swizzled
+//     within the row); V goes global -> registers -> LDS as fp16 V^T with
+//     the keys of every 16-key group permuted to the order in which the
+//     S^T accumulator holds them.  Both are double buffered; K runs two
+//     tiles ahead, V one.
+//   - S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = the
+//     wave's packed query rows, kept in registers): each lane owns the 32
+//     logits of its row that lie in its half, so max and sum are lane-local
+//     plus one swap with the lane 32 apart.  The product for tile n + 1 is
+//     issued in the same instruction stream as the softmax of tile n, so
+//     the matrix cores and the vector unit work side by side.
+//   - online softmax in registers (base-2 exponentials, scale folded in,
+//     lazily moved running max); P is packed to fp16 and the row sum is
+//     taken over the packed values with v_dot2, so numerator and
+//     denominator see the same rounded weights.
+//   - O^T += V^T P^T with v_mfma_f32_32x32x16_f16; P^T comes straight from
+//     the S^T registers.  P and V run in fp16: bf16 V converts exactly in
+//     fp16's normal range (the conversion saturates at +-65504), and fp16
+//     keeps 11 bits of P where bf16 keeps 8.
+#include <type_traits>
+
 #include "device_common.h"
 #include "fi_internal.h"
 
 namespace fi {
 namespace {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsPerWave = 16;
+constexpr int kRowsPerWave = 32;
 constexpr int kTileK = 64;            // keys per KV tile
-constexpr int kVStride = kTileK + 8;  // V^T row stride (elements): 144 B
+constexpr int kVStride = kTileK + 8;  // V^T row stride (elements): 144 B, conflict-free 16-byte reads
 constexpr float kMaxSlack = 8.f;      // log2-domain headroom of the lazily updated running max
 
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
 
 // s_waitcnt with vmcnt <= n and no wait on the other counters (gfx9 encoding)
 #define FI_WAIT_VMCNT(n) \
@@ -54,6 +61,18 @@ typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 // inputs in fp16's normal range; saturates instead of overflowing).
 __device__ __forceinline__ uint32_t pack_f16_rtz(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+
+// v_permlane32_swap on (x, x) leaves x of lane l % 32 in one result and x of
+// lane l % 32 + 32 in the other, in every lane: combining the two gives the
+// pair's max / sum in both halves.
+__device__ __forceinline__ float half_max(float x) {
+  auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
 }
 
 struct PrefillParams {
@@ -79,41 +98,44 @@ struct PrefillParams {
   float inv_cap;
 };
 
-// Position of key k (0..63) of a tile inside a V^T row.  With k = 32 s +
-// 16 h + 4 g + j, the S^T accumulator of lane group g holds keys 4 g + j of
-// both 16-key halves h of k-step s; position 32 s + 8 g + 4 h + j makes those
-// 8 keys contiguous, one 16-byte read of the PV A operand.
-__device__ __forceinline__ int vt_pos(int k) {
-  return (k & ~31) | (((k >> 2) & 3) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
-}
+// Position of key k (0..63) of a tile inside a V^T row: bits 2 and 3
+// swapped.  The S^T accumulator of lane half h holds keys 8 i + 4 h + j
+// (i = 0..3, j = 0..3) of a 32-key block; with the swap, the 8 keys half h
+// feeds to one 16-key k-step of the PV product are contiguous.
+__device__ __forceinline__ int vt_pos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
 #define FI_LDS __attribute__((address_space(3)))
 
 template <int D>
 struct PShape {
-  static constexpr int KRow = D * 2;            // bytes of one K row (no padding)
-  static constexpr int KPiecesRow = D / 8;      // 16-byte pieces of one K row
+  static constexpr int KRow = D * 2;                           // bytes of one K row (no padding)
+  static constexpr int KPiecesRow = D / 8;                     // 16-byte pieces of one K row
   static constexpr int KDma = kTileK * D * 2 / 1024 / kWaves;  // direct-to-LDS K loads per wave
-  static constexpr int KSteps = D / 32;         // MFMA k-steps of Q K^T
-  static constexpr int DBlocks = D / 16;        // 16-dim output blocks
-  static constexpr int VPiecesPerRow = D / 8;   // 16-byte pieces of one V row
+  static constexpr int KeysPerWave = kTileK / kWaves;          // keys of the tile one wave's K loads cover
+  static constexpr int KSteps = D / 16;                        // MFMA k-steps of K Q^T
+  static constexpr int DBlocks = D / 32;                       // 32-dim blocks of O^T
+  static constexpr int VPiecesRow = D / 8;                     // 16-byte pieces of one V row
+  static constexpr int VThreads = 16 * VPiecesRow;             // threads staging V: 4 keys x 1 piece each
 };
 
 template <int D, int G, bool FAST, bool CAP, typename OT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillParams a) {
   using SH = PShape<D>;
-  static_assert(SH::KDma >= 1, "tile too small for the direct-to-LDS split");
-  // K tile: row-major, the 16-byte piece p of key k stored at
-  // p ^ (k % pieces-per-row), which stays inside the row
-  __shared__ __align__(16) uint8_t k_lds[2][kTileK * SH::KRow];
-  __shared__ __align__(16) uint16_t v_lds[2][D * kVStride];
+  static_assert(SH::KDma >= 1 && SH::VThreads <= kThreads, "tile shape");
+  // two buffers each, as separate arrays: the buffer a step uses is a
+  // compile-time choice, so the compiler can tell the direct-to-LDS writes of
+  // one buffer from the reads of the other and need not wait for them
+  __shared__ __align__(16) uint8_t k_lds0[kTileK * SH::KRow];
+  __shared__ __align__(16) uint8_t k_lds1[kTileK * SH::KRow];
+  __shared__ __align__(16) uint16_t v_lds0[D * kVStride];
+  __shared__ __align__(16) uint16_t v_lds1[D * kVStride];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int l16 = lane & 15;
-  const int g4 = lane >> 4;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
   // Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  Give
   // each XCD a contiguous run of (head, worker) slots so that neighbouring
   // workers, which take neighbouring query tiles of the same request, share
@@ -134,18 +156,30 @@ void prefill_kernel(PrefillParams a) {
   float* ws_lse = a.ws + sd[S_WS_LSE];
   const int P = a.P;
   const int Hk = a.Hk;
-  const int64_t tok_stride = (int64_t)Hk * D;
-  const int64_t half_stride = (int64_t)P * tok_stride;
-  const int64_t page_stride = 2 * half_stride;
-  // staging roles: direct-to-LDS K load j of wave w covers tile bytes
-  // (w * KDma + j) * 1024 + 16 lane, i.e. key k_key(j), stored piece lane %
-  // pieces-per-row; V keys 2 (tid % 32) + {0, 1} at piece tid / 32 (threads
-  // past the row idle)
+  const int tok_bytes = Hk * D * 2;
+  const int64_t half_bytes = (int64_t)P * tok_bytes;
+  const int64_t page_bytes = 2 * half_bytes;
+  const uint8_t* kv_head = a.kv + (int64_t)g * D * 2;
+  // staging roles.  K: load j of wave w fills tile bytes (w KDma + j) 1024 +
+  // 16 lane, i.e. key k_key(j) (the wave's keys are 16 consecutive ones),
+  // LDS piece lane % pieces-per-row.  V: thread t < VThreads stages keys
+  // 4 (t % 16) .. + 3 at piece t / 16.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   auto k_key = [&](int j) { return ((wave * SH::KDma + j) * 1024 + 16 * lane) / SH::KRow; };
   const int k_pp = lane % SH::KPiecesRow;
-  const int v_kp = tid & 31;
-  const int v_piece = tid >> 5;
-  const bool v_active = v_piece < SH::VPiecesPerRow;
+  // per-lane part of the K source offset of load j when the wave's 16 keys
+  // sit in one page (tile-independent: key % pieces-per-row depends on the
+  // key's place among the 16 only)
+  uint32_t k_off[SH::KDma];
+#pragma unroll
+  for (int j = 0; j < SH::KDma; ++j) {
+    const int kk = (j * 1024 + 16 * lane) / SH::KRow;
+    k_off[j] = kk * tok_bytes + (k_pp ^ (kk & (SH::KPiecesRow - 1))) * 16;
+  }
+  const int v_kg = tid & 15;
+  const int v_piece = tid >> 4;
+  const bool v_active = SH::VThreads == kThreads || tid < SH::VThreads;
+  const uint32_t pool_lim = a.pool_pages < 0x80000000ll ? (uint32_t)a.pool_pages : 0x80000000u;
 
   const int it_begin = wip[worker];
   const int it_end = wip[worker + 1];
@@ -167,7 +201,7 @@ void prefill_kernel(PrefillParams a) {
     const int ntiles = t1 > t0 ? (t1 - t0 + kTileK - 1) / kTileK : 0;
 
     // this lane's packed row, its token, head and key limit
-    const int r = rb + kRowsPerWave * wave + l16;
+    const int r = rb + kRowsPerWave * wave + l32;
     const bool row_valid = r < re;
     const int rc = row_valid ? r : re - 1;
     const int tok = rc / G;
@@ -177,193 +211,281 @@ void prefill_kernel(PrefillParams a) {
     const int r_first = min(rb + kRowsPerWave * wave, re - 1);
     const int wave_lim_min = min(a.causal ? causal_off + r_first / G + 1 : kv_len, t1);
 
-    // packed query rows as the MFMA B operand (dims 32 ks + 8 g4 .. + 8)
+    // packed query rows as the MFMA B operand (dims 16 ks + 8 hh .. + 8)
     bf16x8_t qp[SH::KSteps];
     {
       const uint8_t* qb = a.q + ((int64_t)(qbase + tok) * a.Hq + head) * D * 2;
 #pragma unroll
       for (int ks = 0; ks < SH::KSteps; ++ks)
-        qp[ks] = __builtin_bit_cast(bf16x8_t, load16(qb + (32 * ks + 8 * g4) * 2));
+        qp[ks] = __builtin_bit_cast(bf16x8_t, load16(qb + (16 * ks + 8 * hh) * 2));
     }
-    f32x4_t oacc[SH::DBlocks];
+    f32x16_t oacc[SH::DBlocks];
 #pragma unroll
-    for (int d = 0; d < SH::DBlocks; ++d) oacc[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int d = 0; d < SH::DBlocks; ++d)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[d][e] = 0.f;
     float m_run = neg_inf();
     float l_part = 0.f;
 
-    // ---- tile staging: K global -> LDS directly, V global -> registers ->
-    // LDS (fp16, transposed); page ids fetched a tile ahead of their loads
-    u32x4_t vreg[2];
-    struct Pages {
-      int k[SH::KDma];
-      int v0, v1;
-    };
-    auto clamp_key = [&](int key) { return key < t1 ? key : t1 - 1; };
+    // ---- staging
     auto page_idx = [&](int key) { return FAST ? key >> a.page_shift : key / P; };
     auto slot_of = [&](int key) { return FAST ? key & (P - 1) : key % P; };
-    auto page_at = [&](int key) -> int {
-      int pg = a.kv_indices[kvb + page_idx(key)];
-      return (uint32_t)pg < (uint64_t)a.pool_pages ? pg : 0;  // never read outside the pool
+    auto clamp_key = [&](int key) { return key < t1 ? key : t1 - 1; };
+    // page ids are loaded raw and checked where they are used, a tile
+    // later, so the load is never waited for early; an id outside the pool
+    // reads page 0 instead
+    auto checked = [&](int pg) -> uint32_t { return (uint32_t)pg < pool_lim ? (uint32_t)pg : 0u; };
+    // With power-of-two pages of >= 16 tokens (FAST) a wave's 16 K keys sit
+    // in one page (tiles start on 16-key boundaries), whose id is then
+    // wave-uniform, and so do a thread's 4 V keys.  K keys past t1 need no
+    // clamping beyond the page (their logits are masked; the page is
+    // valid); V keys are clamped to t1 - 1 so that masked keys still read
+    // finite values (P = 0 times a NaN would not vanish).
+    struct KPages {
+      int id[FAST ? 1 : SH::KDma];
     };
-    auto fetch_pages = [&](int n) -> Pages {
-      Pages pg;
+    struct VPages {
+      int id[FAST ? 1 : 4];
+    };
+    auto fetch_k = [&](int n) -> KPages {
+      KPages pg;
+      const int ts = t0 + n * kTileK;
+      if constexpr (FAST) {
+        const int pi = min(page_idx(ts + wave_u * SH::KeysPerWave), page_idx(t1 - 1));
+        pg.id[0] = n < ntiles ? a.kv_indices[kvb + pi] : 0;  // same in every lane of the wave
+      } else {
 #pragma unroll
-      for (int j = 0; j < SH::KDma; ++j) pg.k[j] = 0;
-      pg.v0 = pg.v1 = 0;
-      if (n < ntiles) {
-        const int ts = t0 + n * kTileK;
-#pragma unroll
-        for (int j = 0; j < SH::KDma; ++j) pg.k[j] = page_at(clamp_key(ts + k_key(j)));
-        pg.v0 = page_at(clamp_key(ts + 2 * v_kp));
-        pg.v1 = page_at(clamp_key(ts + 2 * v_kp + 1));
+        for (int j = 0; j < SH::KDma; ++j) pg.id[j] = n < ntiles ? a.kv_indices[kvb + page_idx(clamp_key(ts + k_key(j)))] : 0;
       }
       return pg;
     };
-    // Keys past t1 read the clamped (valid, finite) last key: their logits
-    // are masked and their P is exactly 0, so neither K nor V needs zeroing.
-    auto load_tile = [&](int n, int buf, const Pages& pg) {
+    auto fetch_v = [&](int n) -> VPages {
+      VPages pg;
       const int ts = t0 + n * kTileK;
+      const bool ok = n < ntiles && v_active;
+      if constexpr (FAST) {
+        pg.id[0] = ok ? a.kv_indices[kvb + page_idx(clamp_key(ts + 4 * v_kg))] : 0;
+      } else {
 #pragma unroll
-      for (int j = 0; j < SH::KDma; ++j) {
-        const int key = k_key(j);
-        const int kc = clamp_key(ts + key);
-        const uint8_t* src = a.kv + ((int64_t)pg.k[j] * page_stride + (int64_t)slot_of(kc) * tok_stride +
-                                     (int64_t)g * D) * 2 + (k_pp ^ (key & (SH::KPiecesRow - 1))) * 16;
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
-                                         (FI_LDS void*)(&k_lds[buf][(wave * SH::KDma + j) * 1024]), 16, 0, 0);
+        for (int j = 0; j < 4; ++j) pg.id[j] = ok ? a.kv_indices[kvb + page_idx(clamp_key(ts + 4 * v_kg + j))] : 0;
       }
-      __builtin_amdgcn_sched_barrier(0);  // K before V: the wait for V then covers K
-      if (v_active) {
+      return pg;
+    };
+    auto dma_k = [&](int n, uint8_t* kb, const KPages& pg) {
+      const int ts = t0 + n * kTileK;
+      if constexpr (FAST) {
+        const int pid = __builtin_amdgcn_readfirstlane(pg.id[0]);
+        const uint8_t* base = kv_head + (int64_t)checked(pid) * page_bytes +
+                              slot_of(ts + wave_u * SH::KeysPerWave) * tok_bytes;
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const int kc = clamp_key(ts + 2 * v_kp + s2);
-          const uint8_t* src = a.kv + ((int64_t)(s2 ? pg.v1 : pg.v0) * page_stride + half_stride +
-                                       (int64_t)slot_of(kc) * tok_stride + (int64_t)g * D) * 2;
-          vreg[s2] = load16(src + v_piece * 16);
+        for (int j = 0; j < SH::KDma; ++j)
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + k_off[j]),
+                                           (FI_LDS void*)(kb + (wave_u * SH::KDma + j) * 1024), 16, 0, 0);
+      } else {
+#pragma unroll
+        for (int j = 0; j < SH::KDma; ++j) {
+          const int key = k_key(j);
+          const int kc = clamp_key(ts + key);
+          const uint8_t* src = kv_head + (int64_t)checked(pg.id[j]) * page_bytes +
+                               (uint32_t)(slot_of(kc) * tok_bytes + (k_pp ^ (key & (SH::KPiecesRow - 1))) * 16);
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                           (FI_LDS void*)(kb + (wave_u * SH::KDma + j) * 1024), 16, 0, 0);
         }
       }
     };
-    auto store_tile = [&](int buf) {
+    u32x4_t vreg[4] = {};
+    auto load_v = [&](int n, const VPages& pg) {
       if (v_active) {
-        const int pos = vt_pos(2 * v_kp);
-        const int dim0 = v_piece * 8;
+        const int ts = t0 + n * kTileK;
+        const uint8_t* base = kv_head + half_bytes + v_piece * 16;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int kc = clamp_key(ts + 4 * v_kg + j);
+          const uint8_t* pbase = base + (int64_t)checked(pg.id[FAST ? 0 : j]) * page_bytes;
+          vreg[j] = load16(pbase + __umul24(slot_of(kc), tok_bytes));
+        }
+      }
+    };
+    auto store_v = [&](uint16_t* vb) {
+      if (v_active) {
+        uint16_t* dst = vb + (8 * v_piece) * kVStride + vt_pos(4 * v_kg);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const uint32_t x = vreg[0][w], y = vreg[1][w];
-          *reinterpret_cast<uint32_t*>(&v_lds[buf][(dim0 + 2 * w) * kVStride + pos]) =
-              pack_f16_rtz(bf16_lo(x), bf16_lo(y));  // dim 2w, keys (2kp, 2kp+1)
-          *reinterpret_cast<uint32_t*>(&v_lds[buf][(dim0 + 2 * w + 1) * kVStride + pos]) =
-              pack_f16_rtz(bf16_hi(x), bf16_hi(y));  // dim 2w + 1
+          u32x2_t lo, hi;  // dims 2w and 2w + 1 of the piece, keys 4 kg .. + 3
+          lo[0] = pack_f16_rtz(bf16_lo(vreg[0][w]), bf16_lo(vreg[1][w]));
+          lo[1] = pack_f16_rtz(bf16_lo(vreg[2][w]), bf16_lo(vreg[3][w]));
+          hi[0] = pack_f16_rtz(bf16_hi(vreg[0][w]), bf16_hi(vreg[1][w]));
+          hi[1] = pack_f16_rtz(bf16_hi(vreg[2][w]), bf16_hi(vreg[3][w]));
+          *reinterpret_cast<u32x2_t*>(dst + (2 * w) * kVStride) = lo;
+          *reinterpret_cast<u32x2_t*>(dst + (2 * w + 1) * kVStride) = hi;
         }
       }
     };
 
-    auto compute_tile = [&](int n, int buf) {
-      const int ts = t0 + n * kTileK;
-      // S^T = K Q^T: 4 blocks of 16 keys
-      f32x4_t sacc[4];
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) sacc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // ---- compute pieces, per 32-key block b of a tile
+    // K operands of block b: key 32 b + l32, dims 16 ks + 8 hh .. + 8
+    auto kread = [&](const uint8_t* kb, int b, u32x4_t (&kop)[SH::KSteps]) {
+      const int key = 32 * b + l32;
+      const uint8_t* krow = kb + key * SH::KRow;
 #pragma unroll
       for (int ks = 0; ks < SH::KSteps; ++ks) {
-        bf16x8_t ka[4];
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          const int key = 16 * mb + l16;
-          const int pp = (4 * ks + g4) ^ (key & (SH::KPiecesRow - 1));
-          ka[mb] = __builtin_bit_cast(bf16x8_t,
-                                      *reinterpret_cast<const u32x4_t*>(&k_lds[buf][key * SH::KRow + pp * 16]));
-        }
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[mb], qp[ks], sacc[mb], 0, 0, 0);
+        const int pp = (2 * ks + hh) ^ (key & (SH::KPiecesRow - 1));
+        kop[ks] = *reinterpret_cast<const u32x4_t*>(krow + pp * 16);
       }
-      // logits: with the cap, into the log2 domain now; without it, the
-      // scale is applied inside the exponent below (order-preserving, > 0)
+    };
+    // S^T block: keys 32 b + 8 i + 4 hh + j of the tile in s[4 i + j]
+    auto qk = [&](const u32x4_t (&kop)[SH::KSteps], f32x16_t& s) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < SH::KSteps; ++ks)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kop[ks]), qp[ks], s, 0, 0, 0);
+    };
+    // V^T operands of block b: dims 32 d + l32, k-steps k of 16 keys
+    auto vread = [&](const uint16_t* vb, int b, u32x4_t (&vop)[2][SH::DBlocks]) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int d = 0; d < SH::DBlocks; ++d)
+          vop[k][d] = *reinterpret_cast<const u32x4_t*>(vb + (32 * d + l32) * kVStride + 32 * b + 16 * k + 8 * hh);
+    };
+    auto pv = [&](const u32x4_t (&vop)[2][SH::DBlocks], const f16x8_t (&pb)[2]) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int d = 0; d < SH::DBlocks; ++d)
+          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, vop[k][d]), pb[k], oacc[d], 0, 0, 0);
+    };
+    const float sc = CAP ? 1.f : a.scale_log2;
+    // logits -> log2 domain (cap) and the mask; only tiles that reach past
+    // the wave's smallest key limit run the masked variant
+    auto prepare = [&](int n, int b, f32x16_t& s, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      const int bs = t0 + n * kTileK + 32 * b;
       if constexpr (CAP) {
         const float c_in = a.scale * a.inv_cap, c_out = a.cap * kLog2e;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sacc[mb][e] = c_out * tanh_from_exp(sacc[mb][e] * c_in);
+        for (int e = 0; e < 16; ++e) s[e] = c_out * tanh_from_exp(s[e] * c_in);
       }
-      const float sc = CAP ? 1.f : a.scale_log2;
-      if (__builtin_expect(ts + kTileK > wave_lim_min, 0)) {  // some key is hidden from some row
+      if constexpr (MASK) {
+        const int rel = lim - bs - 4 * hh;  // key 8 i + j of this half is visible iff < rel
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sacc[mb][e] = ts + 16 * mb + 4 * g4 + e < lim ? sacc[mb][e] : neg_inf();
+        for (int e = 0; e < 16; ++e) s[e] = 8 * (e >> 2) + (e & 3) < rel ? s[e] : neg_inf();
       }
-      float tmax = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
-                         fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
-      tmax = fmaxf(tmax, fmaxf(fmaxf(fmaxf(sacc[2][0], sacc[2][1]), fmaxf(sacc[2][2], sacc[2][3])),
-                               fmaxf(fmaxf(sacc[3][0], sacc[3][1]), fmaxf(sacc[3][2], sacc[3][3]))));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      tmax *= sc;  // into the log2 domain
-      // the reference max only moves when a tile beats it by more than 2^8
+    };
+    // online softmax of a prepared block: P^T (fp16) for its 2 PV k-steps;
+    // returns the factor the accumulator must be rescaled by
+    auto softmax = [&](f32x16_t& s, f16x8_t (&pb)[2]) -> float {
+      float tm = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+      for (int e = 3; e < 15; e += 2) tm = fmaxf(fmaxf(tm, s[e]), s[e + 1]);
+      tm = fmaxf(tm, s[15]);
+      const float tmax = half_max(tm) * sc;
+      // the reference max only moves when a block beats it by more than 2^8
       const float m_new = tmax > m_run + kMaxSlack ? tmax : m_run;
       const float m_use = m_new == neg_inf() ? 0.f : m_new;
       const float alpha = fast_exp2(m_run - m_use);
       m_run = m_new;
+      const f16x2_t ones = {(_Float16)1.f, (_Float16)1.f};
+      float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int k = 0; k < 2; ++k) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sacc[mb][e] = fast_exp2(fmaf(sacc[mb][e], sc, -m_use));
-      const f32x4_t s01 = sacc[0] + sacc[1], s23 = sacc[2] + sacc[3];
-      const f32x4_t s4 = s01 + s23;
-      l_part = l_part * alpha + ((s4[0] + s4[1]) + (s4[2] + s4[3]));
+        for (int i = 0; i < 4; ++i) {
+          const float p0 = fast_exp2(fmaf(s[8 * k + 2 * i], sc, -m_use));
+          const float p1 = fast_exp2(fmaf(s[8 * k + 2 * i + 1], sc, -m_use));
+          const f16x2_t pp = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+          pb[k][2 * i] = pp[0];
+          pb[k][2 * i + 1] = pp[1];
+          if (i & 1) ls1 = __builtin_amdgcn_fdot2(pp, ones, ls1, false);
+          else ls0 = __builtin_amdgcn_fdot2(pp, ones, ls0, false);
+        }
+      }
+      l_part = l_part * alpha + (ls0 + ls1);
+      return alpha;
+    };
+    auto rescale = [&](float alpha) {
       if (__builtin_expect(__any(alpha != 1.f), 0)) {  // wave-uniform; rare once the max settles
 #pragma unroll
         for (int d = 0; d < SH::DBlocks; ++d) oacc[d] *= alpha;
       }
-      // O^T += V^T P^T over 2 k-steps of 32 keys
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        f16x8_t pb8;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pb8[i] = (_Float16)sacc[2 * ks][i];
-          pb8[4 + i] = (_Float16)sacc[2 * ks + 1][i];
-        }
-#pragma unroll
-        for (int d0 = 0; d0 < SH::DBlocks; d0 += 4) {
-          f16x8_t va[4];
-#pragma unroll
-          for (int d = 0; d < 4; ++d)
-            va[d] = __builtin_bit_cast(
-                f16x8_t, *reinterpret_cast<const u32x4_t*>(
-                             &v_lds[buf][(16 * (d0 + d) + l16) * kVStride + 32 * ks + 8 * g4]));
-#pragma unroll
-          for (int d = 0; d < 4; ++d)
-            oacc[d0 + d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[d], pb8, oacc[d0 + d], 0, 0, 0);
-        }
-      }
     };
 
+    // ---- pipeline.  Per tile n (buffers chosen at compile time):
+    //   K(b0) reads | QK(b0) with the K(b1) reads and the issue of tile
+    //   n + 1's loads | QK(b1) with softmax(b0) and the V(b0) reads |
+    //   PV(b0) with softmax(b1) and the V(b1) reads | PV(b1) with the fp16
+    //   conversion of V(n + 1) | one barrier.
     // The compiler does not track direct-to-LDS loads: every thread waits
-    // for all of its loads before the barrier that publishes a tile.
-    Pages pg_next = fetch_pages(1);
+    // for all of its loads before the barrier.
+    __syncthreads();  // the previous item's last reads of both buffers are done
+    KPages pk = fetch_k(0);
+    VPages pv_ids = fetch_v(0);
     if (ntiles > 0) {
-      load_tile(0, 0, fetch_pages(0));
-      store_tile(0);
+      dma_k(0, k_lds0, pk);
+      load_v(0, pv_ids);
     }
+    pk = fetch_k(1);
+    pv_ids = fetch_v(1);
+    if (ntiles > 0) store_v(v_lds0);
     FI_WAIT_VMCNT(0);
     __syncthreads();
-    for (int n = 0; n < ntiles; ++n) {
-      const int buf = n & 1;
-      if (n + 1 < ntiles) load_tile(n + 1, buf ^ 1, pg_next);
-      pg_next = fetch_pages(n + 2);  // page ids one tile ahead of the loads
-      compute_tile(n, buf);  // fully masked tiles of a wave give p = 0 and leave its state as is
-      if (n + 1 < ntiles) store_tile(buf ^ 1);
+    // fences: P must be materialised before the (rare) rescale branch, so
+    // the exponentials stay next to the products they overlap with
+    auto fence = [](const f16x8_t (&pb)[2]) {
+      asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, pb[0])), "v"(__builtin_bit_cast(u32x4_t, pb[1])));
+    };
+    // Loads for tile n + 1 are issued even past the last tile (page ids of
+    // tiles past the end read as 0, a valid page): nothing reads that data,
+    // and the body stays free of branches.
+    auto step = [&](int n, auto cur, auto mask_tag) {
+      constexpr bool B1 = decltype(cur)::value;
+      uint8_t* kb = B1 ? k_lds1 : k_lds0;
+      uint8_t* kb_next = B1 ? k_lds0 : k_lds1;
+      uint16_t* vb = B1 ? v_lds1 : v_lds0;
+      uint16_t* vb_next = B1 ? v_lds0 : v_lds1;
+      u32x4_t kop0[SH::KSteps], kop1[SH::KSteps];
+      u32x4_t vop0[2][SH::DBlocks], vop1[2][SH::DBlocks];
+      f32x16_t s0, s1;
+      f16x8_t p0[2], p1[2];
+      kread(kb, 0, kop0);
+      kread(kb, 1, kop1);
+      dma_k(n + 1, kb_next, pk);
+      load_v(n + 1, pv_ids);
+      pk = fetch_k(n + 2);
+      pv_ids = fetch_v(n + 2);
+      qk(kop0, s0);
+      prepare(n, 0, s0, mask_tag);
+      // QK(b1) + softmax(b0) + V(b0) reads
+      qk(kop1, s1);
+      vread(vb, 0, vop0);
+      const float a0 = softmax(s0, p0);
+      fence(p0);
+      rescale(a0);
+      prepare(n, 1, s1, mask_tag);
+      // PV(b0) + softmax(b1) + V(b1) reads
+      pv(vop0, p0);
+      vread(vb, 1, vop1);
+      const float a1 = softmax(s1, p1);
+      fence(p1);
+      rescale(a1);
+      // PV(b1) + the conversion of the next V tile
+      pv(vop1, p1);
+      store_v(vb_next);
       FI_WAIT_VMCNT(0);
       __syncthreads();
+    };
+    auto step_any = [&](int n, auto cur) {
+      if (t0 + n * kTileK + kTileK > wave_lim_min) step(n, cur, std::true_type{});
+      else step(n, cur, std::false_type{});
+    };
+    for (int n = 0; n < ntiles; n += 2) {
+      step_any(n, std::false_type{});
+      if (n + 1 < ntiles) step_any(n + 1, std::true_type{});
     }
 
-    // ---- epilogue: normalise and write this lane's row (dims 16 d + 4 g4 + e)
-    float l_tot = l_part + __shfl_xor(l_part, 16);
-    l_tot += __shfl_xor(l_tot, 32);
+    // ---- epilogue: normalise and write this lane's row (dims 32 d + 8 i + 4 hh + j)
+    const float l_tot = half_sum(l_part);
     const bool empty = m_run == neg_inf() || !(l_tot > 0.f);
     const float inv = empty ? 0.f : 1.f / l_tot;
     const float lse_nat = empty ? neg_inf() : (m_run + fast_log2(l_tot)) * kLn2;
@@ -371,26 +493,32 @@ void prefill_kernel(PrefillParams a) {
       if (slot < 0) {
         const int64_t orow = (int64_t)(qbase + tok) * a.Hq + head;
 #pragma unroll
-        for (int d = 0; d < SH::DBlocks; ++d) {
-          const int dim = 16 * d + 4 * g4;
-          const float v0 = oacc[d][0] * inv, v1 = oacc[d][1] * inv;
-          const float v2 = oacc[d][2] * inv, v3 = oacc[d][3] * inv;
-          if constexpr (OT::kBytes == 2) {
-            u32x2_t w;
-            w[0] = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
-            w[1] = f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16);
-            *reinterpret_cast<u32x2_t*>(a.o + (orow * D + dim) * 2) = w;
-          } else {
-            *reinterpret_cast<f32x4_t*>(a.o + (orow * D + dim) * 4) = f32x4_t{v0, v1, v2, v3};
+        for (int d = 0; d < SH::DBlocks; ++d)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int dim = 32 * d + 8 * i + 4 * hh;
+            const float v0 = oacc[d][4 * i] * inv, v1 = oacc[d][4 * i + 1] * inv;
+            const float v2 = oacc[d][4 * i + 2] * inv, v3 = oacc[d][4 * i + 3] * inv;
+            if constexpr (OT::kBytes == 2) {
+              u32x2_t w;
+              w[0] = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
+              w[1] = f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16);
+              *reinterpret_cast<u32x2_t*>(a.o + (orow * D + dim) * 2) = w;
+            } else {
+              *reinterpret_cast<f32x4_t*>(a.o + (orow * D + dim) * 4) = f32x4_t{v0, v1, v2, v3};
+            }
           }
-        }
-        if (a.lse && g4 == 0) a.lse[orow] = lse_nat;
+        if (a.lse && hh == 0) a.lse[orow] = lse_nat;
       } else {
         const int64_t prow = ((int64_t)slot * Hk + g) * kMaxTileRows + (r - rb);
 #pragma unroll
         for (int d = 0; d < SH::DBlocks; ++d)
-          *reinterpret_cast<f32x4_t*>(ws_o + prow * D + 16 * d + 4 * g4) = oacc[d] * inv;
-        if (g4 == 0) ws_lse[prow] = lse_nat;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<f32x4_t*>(ws_o + prow * D + 32 * d + 8 * i + 4 * hh) =
+                f32x4_t{oacc[d][4 * i] * inv, oacc[d][4 * i + 1] * inv, oacc[d][4 * i + 2] * inv,
+                        oacc[d][4 * i + 3] * inv};
+        if (hh == 0) ws_lse[prow] = lse_nat;
       }
     }
   }
