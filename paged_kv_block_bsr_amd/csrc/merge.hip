@@ -31,11 +31,12 @@ struct MergeParams {
 
 constexpr int kMergeRows = 16;  // packed rows per merge block (grid z covers a 128-row tile)
 
-// Block (task, g, z) merges rows 16 z .. 16 z + 15 of split row `task`:
-//  1. per row, 16 threads reduce the slots' lse to the max M and 1 / L;
-//  2. threads take (row, 4-dim chunk) units; when there are fewer units than
-//     threads, the slots are also divided among thread groups and the group
-//     sums are added through LDS, so long slot lists are read in parallel.
+// Block (task, g, z) merges rows 16 z .. 16 z + 15 of split row `task`.
+// Threads take (row, 4-dim chunk) units; when there are fewer units than
+// threads, the slots are also divided among thread groups.  Each thread
+// folds its slots into a running (max, sum, weighted o) state as it reads
+// them -- lse and o of a slot are loaded together, so a block needs one
+// round trip to memory -- and the group states are composed through LDS.
 __global__ __launch_bounds__(kThreads) void merge_partials_kernel(MergeParams a) {
   const int32_t* sd = a.plan + a.stream_at;
   const int task = blockIdx.x;
@@ -58,51 +59,13 @@ __global__ __launch_bounds__(kThreads) void merge_partials_kernel(MergeParams a)
   const int qbase = a.qo_indptr ? a.qo_indptr[req] : req;
   const int D = a.D, G = a.G;
   const int tid = threadIdx.x;
-  auto lse_at = [&](int s, int r) { return wl[((int64_t)s * a.Hk + g) * stride + r]; };
 
-  __shared__ float sM[kMergeRows], sInv[kMergeRows];
-  __shared__ f32x4_t red[kThreads];
-  {
-    const int rr = tid >> 4, l16 = tid & 15;
-    float M = neg_inf();
-    if (rr < nr)
-      for (int s = s0 + l16; s < s1; s += 16) M = fmaxf(M, lse_at(s, r0 + rr));
-#pragma unroll
-    for (int off = 8; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 16));
-    float L = 0.f;
-    if (rr < nr && M != neg_inf())
-      for (int s = s0 + l16; s < s1; s += 16) L += __expf(lse_at(s, r0 + rr) - M);
-#pragma unroll
-    for (int off = 8; off > 0; off >>= 1) L += __shfl_xor(L, off, 16);
-    if (rr < nr && l16 == 0) {
-      sM[rr] = M;
-      sInv[rr] = M == neg_inf() ? 0.f : 1.f / L;
-    }
-  }
-  __syncthreads();
-  const int chunks = D / 4;
-  const int U = nr * chunks;  // (row, 4-dim chunk) units
-  int UP = 1;
-  while (UP < U) UP <<= 1;
-  const int ngroups = UP >= kThreads ? 1 : kThreads / UP;
-  const int sg = UP >= kThreads ? 0 : tid / UP;
-  for (int u = (UP >= kThreads ? tid : tid % UP); u < U; u += (UP >= kThreads ? kThreads : UP)) {
-    const int rr = u / chunks, c = u % chunks;
-    const float M = sM[rr], inv = sInv[rr];
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    if (M != neg_inf()) {
-#pragma unroll 4
-      for (int s = s0 + sg; s < s1; s += ngroups) {
-        const int64_t pr = ((int64_t)s * a.Hk + g) * stride + r0 + rr;
-        const float w = __expf(wl[pr] - M) * inv;
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(wo + pr * D + 4 * c);
-        acc += w * v;
-      }
-    }
-    if (ngroups > 1) {
-      red[tid] = acc;
-      break;  // one unit per thread when the slots are split among groups
-    }
+  __shared__ f32x4_t red_acc[kThreads];
+  __shared__ float red_m[kThreads], red_l[kThreads];
+  auto write_out = [&](int rr, int c, f32x4_t acc, float m, float l) {
+    const bool empty = m == neg_inf() || !(l > 0.f);
+    const float inv = empty ? 0.f : 1.f / l;
+    acc *= inv;
     const int packed = rb + r0 + rr;
     const int64_t orow = (int64_t)(qbase + packed / G) * a.Hq + g * G + packed % G;
     if (a.out_bf16) {
@@ -113,26 +76,57 @@ __global__ __launch_bounds__(kThreads) void merge_partials_kernel(MergeParams a)
     } else {
       *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.o) + orow * D + 4 * c) = acc;
     }
-    if (a.lse && c == 0) a.lse[orow] = M == neg_inf() ? neg_inf() : M + __logf(1.f / inv);
+    if (a.lse && c == 0) a.lse[orow] = empty ? neg_inf() : m + __logf(l);
+  };
+  const int chunks = D / 4;
+  const int U = nr * chunks;  // (row, 4-dim chunk) units
+  int UP = 1;
+  while (UP < U) UP <<= 1;
+  const int ngroups = UP >= kThreads ? 1 : kThreads / UP;
+  const int sg = UP >= kThreads ? 0 : tid / UP;
+  for (int u = (UP >= kThreads ? tid : tid % UP); u < U; u += (UP >= kThreads ? kThreads : UP)) {
+    const int rr = u / chunks, c = u % chunks;
+    float m = neg_inf(), l = 0.f;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int s = s0 + sg; s < s1; s += ngroups) {
+      const int64_t pr = ((int64_t)s * a.Hk + g) * stride + r0 + rr;
+      const float x = wl[pr];
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(wo + pr * D + 4 * c);
+      if (x > m) {  // a new running max: rescale what is there (exp(-inf) = 0 on the first slot)
+        const float r = __expf(m - x);
+        acc *= r;
+        l *= r;
+        m = x;
+      }
+      const float w = x == neg_inf() ? 0.f : __expf(x - m);
+      acc += w * v;
+      l += w;
+    }
+    if (ngroups > 1) {
+      red_acc[tid] = acc;
+      red_m[tid] = m;
+      red_l[tid] = l;
+      break;  // one unit per thread when the slots are split among groups
+    }
+    write_out(rr, c, acc, m, l);
   }
   if (ngroups > 1) {
     __syncthreads();
     if (tid < U) {
-      f32x4_t acc = red[tid];
-      for (int k = 1; k < ngroups; ++k) acc += red[tid + k * UP];
-      const int rr = tid / chunks, c = tid % chunks;
-      const float M = sM[rr], inv = sInv[rr];
-      const int packed = rb + r0 + rr;
-      const int64_t orow = (int64_t)(qbase + packed / G) * a.Hq + g * G + packed % G;
-      if (a.out_bf16) {
-        uint32_t lo = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
-        uint32_t hi = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
-        reinterpret_cast<uint32_t*>(a.o)[(orow * D + 4 * c) / 2] = lo;
-        reinterpret_cast<uint32_t*>(a.o)[(orow * D + 4 * c) / 2 + 1] = hi;
-      } else {
-        *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.o) + orow * D + 4 * c) = acc;
+      float M = red_m[tid];
+      for (int k = 1; k < ngroups; ++k) M = fmaxf(M, red_m[tid + k * UP]);
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      float L = 0.f;
+      if (M != neg_inf()) {
+        for (int k = 0; k < ngroups; ++k) {
+          const float mk = red_m[tid + k * UP];
+          const float w = mk == neg_inf() ? 0.f : __expf(mk - M);
+          acc += w * red_acc[tid + k * UP];
+          L += w * red_l[tid + k * UP];
+        }
       }
-      if (a.lse && c == 0) a.lse[orow] = M == neg_inf() ? neg_inf() : M + __logf(1.f / inv);
+      write_out(tid / chunks, tid % chunks, acc, M, L);
     }
   }
 }
