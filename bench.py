@@ -281,6 +281,18 @@ def secondary_measurements(args):
     return out
 
 
+def prefill_only(args):
+    """The prefill slice of the mixed ragged step alone, timed like the side
+    measurement (one plan, then the run call on its stream)."""
+    import workloads as wl
+    ps = prefill_slice(wl.mixed_ragged_step())
+    ms, plan = time_batch_call(ps, args.side_steps, 3)
+    fl = prefill_flops(ps)
+    return {"workload": "mixed_ragged_step prefill requests (16 causal prefills)", "ms": round(ms, 4),
+            "tflops": round(fl / (ms * 1e-3) / 1e12, 2), "flops": fl,
+            "prefill_items": int(plan.info.prefill_items), "steps": args.side_steps}
+
+
 def time_cascade(cb, steps, warmup):
     import torch
 
@@ -385,8 +397,9 @@ def main():
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the prefill / mixed / cascade side measurements")
     ap.add_argument("--side-steps", type=int, default=20)
-    ap.add_argument("--mode", default="bench", choices=["bench", "secondary", "calibrate"],
+    ap.add_argument("--mode", default="bench", choices=["bench", "secondary", "prefill", "calibrate"],
                     help="secondary: only the prefill / mixed / cascade measurements; "
+                         "prefill: only the prefill-slice timing (for profiling that kernel); "
                          "calibrate: only the plain copy / streaming-sum kernels")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -399,6 +412,9 @@ def main():
         return
     if args.mode == "calibrate":
         print(json.dumps(calibrate()), flush=True)
+        return
+    if args.mode == "prefill":
+        print(json.dumps(prefill_only(args)), flush=True)
         return
     result, b, nbytes = run_decode_bench(args)
     if not args.no_secondary:
