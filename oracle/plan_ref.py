@@ -226,6 +226,16 @@ def plan(qo_indptr, kv_indptr, kv_last_page_len, *, page_size, num_qo_heads, num
         buf.extend(st["merge_indptr"])
         st["off_split"] = len(buf)
         buf.extend(st["split_rows"])
+        # per-item copy of what a kernel needs about the item's request and
+        # row, so that one load per item replaces a chain of dependent ones
+        st["item_meta"] = []
+        for (r, pb, pe, slot) in st["items"]:
+            req, rb, re, _ = st["rows"][r]
+            qb = req if qo_indptr is None else qo_indptr[req]
+            st["item_meta"].append((req, kv_indptr[req], kv_len[req], qb, qo_len[req], rb, re, 0))
+        st["off_item_meta"] = len(buf)
+        for m in st["item_meta"]:
+            buf.extend(m)
     head = [MAGIC, VERSION, len(buf), B, sum(qo_len), Hq, Hk, D, P, int(bool(causal)), G,
             ws_total]
     buf[:len(head)] = head
@@ -233,7 +243,7 @@ def plan(qo_indptr, kv_indptr, kv_last_page_len, *, page_size, num_qo_heads, num
         desc = [st["W"], st["S"], st["BR"], len(st["rows"]), len(st["items"]), st["n_slots"],
                 len(st["split_rows"]), st["slot_cap"], st["off_rows"], st["off_items"],
                 st["off_wip"], st["off_merge_indptr"], st["off_split"], st["ws_off_o"],
-                st["ws_off_lse"], st["kind"], 0, 0, 0, 0]
+                st["ws_off_lse"], st["kind"], st["off_item_meta"], 0, 0, 0]
         buf[at:at + STREAM_DESC_INTS] = desc
     result = dict(B=B, total_qo=sum(qo_len), G=G, ws_floats=ws_total, decode=streams[0],
                   prefill=streams[1], buf=buf, kv_len=kv_len, qo_len=qo_len)

@@ -88,7 +88,7 @@ __device__ __forceinline__ f32x4_t qk_mfma(const u32x4_t (&kp)[NK], const u32x4_
 template <typename OT>
 __device__ __forceinline__ void store_out(uint8_t* base, int64_t idx, float v) {
   if constexpr (OT::kBytes == 2)
-    reinterpret_cast<uint16_t*>(base)[idx] = (uint16_t)f32_to_bf16_bits(v);
+    reinterpret_cast<uint16_t*>(base)[idx] = (uint16_t)pack_bf16x2(v, 0.f);
   else
     reinterpret_cast<float*>(base)[idx] = v;
 }
@@ -110,8 +110,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams a) {
   const int worker = blockIdx.x;
   const int g = blockIdx.y;
   const int32_t* sd = a.plan + a.stream_at;
-  const int32_t* rows = a.plan + sd[S_OFF_ROWS];
   const int32_t* items = a.plan + sd[S_OFF_ITEMS];
+  const int32_t* meta = a.plan + sd[S_OFF_META];
   const int32_t* wip = a.plan + sd[S_OFF_WIP];
   float* ws_o = a.ws + sd[S_WS_O];
   float* ws_lse = a.ws + sd[S_WS_LSE];
@@ -131,17 +131,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams a) {
   const int it_begin = wip[worker];
   const int it_end = wip[worker + 1];
   for (int it = it_begin; it < it_end; ++it) {
-    const int row = items[4 * it + 0];
+    // the item and its request's record: two independent loads
     const int pb = items[4 * it + 1];
     const int pe = items[4 * it + 2];
     const int slot = items[4 * it + 3];
-    const int req = rows[4 * row + 0];
-    const int kvb = a.kv_indptr[req];
-    const int npg = a.kv_indptr[req + 1] - kvb;
-    const int kv_len = npg ? (npg - 1) * P + a.kv_last[req] : 0;
+    const int32_t* im = meta + kMetaInts * it;
+    const int kvb = im[M_KVB];
+    const int kv_len = im[M_KVLEN];
     const int t0 = pb * P;
     const int t1 = min(pe * P, kv_len);
-    const int qrow = a.qo_indptr ? a.qo_indptr[req] : req;
+    const int qrow = im[M_QOBASE];
     const int nch = t1 > t0 ? (t1 - t0 + kChunk - 1) / kChunk : 0;
 
     // packed query heads as MFMA B operand: column hS, dims of slice kq
@@ -378,8 +377,6 @@ typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 #define FI_WAIT_VMCNT(n) \
   __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
-__device__ __forceinline__ uint32_t bf16_bits_rne(float f) { return f32_to_bf16_bits(f); }
-
 template <int D, int G, typename OT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void decode_mfma_kernel(DecodeParams a) {
@@ -400,8 +397,8 @@ void decode_mfma_kernel(DecodeParams a) {
   const int worker = blockIdx.x;
   const int g = blockIdx.y;
   const int32_t* sd = a.plan + a.stream_at;
-  const int32_t* rows = a.plan + sd[S_OFF_ROWS];
   const int32_t* items = a.plan + sd[S_OFF_ITEMS];
+  const int32_t* meta = a.plan + sd[S_OFF_META];
   const int32_t* wip = a.plan + sd[S_OFF_WIP];
   float* ws_o = a.ws + sd[S_WS_O];
   float* ws_lse = a.ws + sd[S_WS_LSE];
@@ -426,17 +423,16 @@ void decode_mfma_kernel(DecodeParams a) {
   const int it_begin = wip[worker];
   const int it_end = wip[worker + 1];
   for (int it = it_begin; it < it_end; ++it) {
-    const int row = items[4 * it + 0];
+    // the item and its request's record: two independent loads
     const int pb = items[4 * it + 1];
     const int pe = items[4 * it + 2];
     const int slot = items[4 * it + 3];
-    const int req = rows[4 * row + 0];
-    const int kvb = a.kv_indptr[req];
-    const int npg = a.kv_indptr[req + 1] - kvb;
-    const int kv_len = npg ? (npg - 1) * P + a.kv_last[req] : 0;
+    const int32_t* im = meta + kMetaInts * it;
+    const int kvb = im[M_KVB];
+    const int kv_len = im[M_KVLEN];
     const int t0 = pb * P;
     const int t1 = min(pe * P, kv_len);
-    const int qrow = a.qo_indptr ? a.qo_indptr[req] : req;
+    const int qrow = im[M_QOBASE];
     const int nch = t1 > t0 ? (t1 - t0 + kChunk - 1) / kChunk : 0;
 
     u32x4_t qp[NK];
@@ -515,15 +511,12 @@ void decode_mfma_kernel(DecodeParams a) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) oacc[b] *= alpha;
       }
-      // P^T as bf16 hi + lo parts
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        hi[r] = bf16_bits_rne(p[r]);
-        lo[r] = bf16_bits_rne(p[r] - __uint_as_float(hi[r] << 16));
-      }
-      const s16x4_t bhi = __builtin_bit_cast(s16x4_t, u32x2_t{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)});
-      const s16x4_t blo = __builtin_bit_cast(s16x4_t, u32x2_t{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)});
+      // P^T as bf16 hi + lo parts (lo = the rounding remainder of hi)
+      const uint32_t h01 = pack_bf16x2(p[0], p[1]), h23 = pack_bf16x2(p[2], p[3]);
+      const uint32_t l01 = pack_bf16x2(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
+      const uint32_t l23 = pack_bf16x2(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
+      const s16x4_t bhi = __builtin_bit_cast(s16x4_t, u32x2_t{h01, h23});
+      const s16x4_t blo = __builtin_bit_cast(s16x4_t, u32x2_t{l01, l23});
       const FI_LDS uint8_t* stage = (const FI_LDS uint8_t*)(&vring[wave][st][0]);
 #pragma unroll
       for (int b = 0; b < NB; ++b) {

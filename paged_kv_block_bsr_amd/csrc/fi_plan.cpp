@@ -180,7 +180,7 @@ int plan_bounds(int32_t B, int64_t total_qo, int32_t Hq, int32_t Hk, int32_t D, 
   const int64_t rows_p = ceil_div(total_qo * G, 16) + B;
   auto stream_ints = [](int64_t rows, int64_t W) {
     int64_t items = rows + W - 1;
-    return 4 * rows + 4 * items + (W + 1) + (rows + 1) + rows;
+    return 4 * rows + (4 + kMetaInts) * items + (W + 1) + (rows + 1) + rows;
   };
   if (plan_ints) *plan_ints = kHeaderInts + stream_ints(rows_d, Wd) + stream_ints(rows_p, Wp);
   int64_t off[4], total;
@@ -251,7 +251,7 @@ int build_plan(const fi_plan_in* inp, int32_t* buf, int64_t capacity, fi_plan_in
   // P9: size, then emit
   int64_t need = kHeaderInts;
   for (auto& s : st)
-    need += 4 * (int64_t)s.rows.size() + 4 * (int64_t)s.item_row.size() + (s.W + 1) +
+    need += 4 * (int64_t)s.rows.size() + (4 + kMetaInts) * (int64_t)s.item_row.size() + (s.W + 1) +
             ((int64_t)s.rows.size() + 1) + (int64_t)s.split.size();
   if (!buf || capacity < need)
     return set_error(FI_ERR_WORKSPACE_TOO_SMALL, "fi_plan: plan buffer holds %lld ints, needs %lld",
@@ -294,6 +294,18 @@ int build_plan(const fi_plan_in* inp, int32_t* buf, int64_t capacity, fi_plan_in
     for (int32_t v : s.merge) buf[pos++] = v;
     d[S_OFF_SPLIT] = (int32_t)pos;
     for (int32_t v : s.split) buf[pos++] = v;
+    d[S_OFF_META] = (int32_t)pos;
+    for (int64_t j = 0; j < ni; ++j) {
+      const Row& r = s.rows[s.item_row[j]];
+      buf[pos++] = r.req;
+      buf[pos++] = in.kv_indptr[r.req];
+      buf[pos++] = (int32_t)kv[r.req];
+      buf[pos++] = in.qo_indptr ? in.qo_indptr[r.req] : r.req;
+      buf[pos++] = (int32_t)qo[r.req];
+      buf[pos++] = r.rb;
+      buf[pos++] = r.re;
+      buf[pos++] = 0;
+    }
   }
   buf[H_MAGIC] = kPlanMagic;
   buf[H_VERSION] = kPlanVersion;

@@ -69,8 +69,8 @@ __global__ __launch_bounds__(kThreads) void merge_partials_kernel(MergeParams a)
     const int packed = rb + r0 + rr;
     const int64_t orow = (int64_t)(qbase + packed / G) * a.Hq + g * G + packed % G;
     if (a.out_bf16) {
-      uint32_t lo = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
-      uint32_t hi = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
+      const uint32_t lo = pack_bf16x2(acc[0], acc[1]);
+      const uint32_t hi = pack_bf16x2(acc[2], acc[3]);
       reinterpret_cast<uint32_t*>(a.o)[(orow * D + 4 * c) / 2] = lo;
       reinterpret_cast<uint32_t*>(a.o)[(orow * D + 4 * c) / 2 + 1] = hi;
     } else {
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void merge_state_kernel(const uint8_t* va
       }
       const float r = empty ? 0.f : (wa * x + wb * y) * inv;
       if constexpr (OT::kBytes == 2)
-        reinterpret_cast<uint16_t*>(vo)[i] = (uint16_t)f32_to_bf16_bits(r);
+        reinterpret_cast<uint16_t*>(vo)[i] = (uint16_t)pack_bf16x2(r, 0.f);
       else
         reinterpret_cast<float*>(vo)[i] = r;
     }

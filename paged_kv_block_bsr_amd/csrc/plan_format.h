@@ -9,6 +9,11 @@
 //   wip    [W+1]        items of worker w are items[wip[w] .. wip[w+1])
 //   merge  [n_rows+1]   slots of row r are merge[r] .. merge[r+1]
 //   split  [n_split]    rows with two or more items, in row order
+//   meta   [n_items][8] {request, kv_indptr[request], kv_len, qo_base, qo_len,
+//                        packed_row_begin, packed_row_end, 0} of each item's
+//                        request and row (qo_base = qo_indptr[request], or the
+//                        request itself for a decode-only batch), so a kernel
+//                        reads one record per item instead of a dependent chain
 // A packed row r of a request stands for (token r / G, head-in-group r % G);
 // a decode row packs the G query heads of one KV head.  Page indices in
 // items are local to the request (the kernel adds kv_indptr[request]).
@@ -24,6 +29,9 @@ namespace fi {
 constexpr int32_t kPlanMagic = 0x31504946;  // "FIP1"
 constexpr int32_t kPlanVersion = 1;
 constexpr int kHeaderInts = 64;
+constexpr int kMetaInts = 8;  // ints per item_meta record
+// item_meta fields
+enum : int { M_REQ = 0, M_KVB = 1, M_KVLEN = 2, M_QOBASE = 3, M_QOLEN = 4, M_RB = 5, M_RE = 6 };
 constexpr int kMaxTileRows = 128;
 
 // header words
@@ -62,6 +70,7 @@ enum : int {
   S_WS_O = 13,
   S_WS_LSE = 14,
   S_KIND = 15,
+  S_OFF_META = 16,
   kStreamDescInts = 20,
 };
 

@@ -149,8 +149,8 @@ void prefill_kernel(PrefillParams a) {
     worker = s % a.workers;
   }
   const int32_t* sd = a.plan + a.stream_at;
-  const int32_t* rows = a.plan + sd[S_OFF_ROWS];
   const int32_t* items = a.plan + sd[S_OFF_ITEMS];
+  const int32_t* meta = a.plan + sd[S_OFF_META];
   const int32_t* wip = a.plan + sd[S_OFF_WIP];
   float* ws_o = a.ws + sd[S_WS_O];
   float* ws_lse = a.ws + sd[S_WS_LSE];
@@ -184,18 +184,17 @@ void prefill_kernel(PrefillParams a) {
   const int it_begin = wip[worker];
   const int it_end = wip[worker + 1];
   for (int it = it_begin; it < it_end; ++it) {
-    const int row = items[4 * it + 0];
+    // the item and its request's record: two independent loads
     const int pb = items[4 * it + 1];
     const int pe = items[4 * it + 2];
     const int slot = items[4 * it + 3];
-    const int req = rows[4 * row + 0];
-    const int rb = rows[4 * row + 1];
-    const int re = rows[4 * row + 2];
-    const int kvb = a.kv_indptr[req];
-    const int npg = a.kv_indptr[req + 1] - kvb;
-    const int kv_len = npg ? (npg - 1) * P + a.kv_last[req] : 0;
-    const int qbase = a.qo_indptr[req];
-    const int qo_len = a.qo_indptr[req + 1] - qbase;
+    const int32_t* im = meta + kMetaInts * it;
+    const int rb = im[M_RB];
+    const int re = im[M_RE];
+    const int kvb = im[M_KVB];
+    const int kv_len = im[M_KVLEN];
+    const int qbase = im[M_QOBASE];
+    const int qo_len = im[M_QOLEN];
     const int t0 = pb * P;
     const int t1 = min(pe * P, kv_len);
     const int ntiles = t1 > t0 ? (t1 - t0 + kTileK - 1) / kTileK : 0;
@@ -501,8 +500,8 @@ void prefill_kernel(PrefillParams a) {
             const float v2 = oacc[d][4 * i + 2] * inv, v3 = oacc[d][4 * i + 3] * inv;
             if constexpr (OT::kBytes == 2) {
               u32x2_t w;
-              w[0] = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
-              w[1] = f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16);
+              w[0] = pack_bf16x2(v0, v1);
+              w[1] = pack_bf16x2(v2, v3);
               *reinterpret_cast<u32x2_t*>(a.o + (orow * D + dim) * 2) = w;
             } else {
               *reinterpret_cast<f32x4_t*>(a.o + (orow * D + dim) * 4) = f32x4_t{v0, v1, v2, v3};

@@ -56,6 +56,7 @@ def _compare(qo_indptr, kv_indptr, last, **kw):
         assert d[name]["wip"] == st["wip"]
         assert d[name]["merge_indptr"] == st["merge_indptr"]
         assert d[name]["split_rows"] == st["split_rows"]
+        assert d[name]["item_meta"] == [tuple(m) for m in st["item_meta"]]
     assert plan.float_ws_bytes == 4 * res["ws_floats"]
     return plan, res
 

@@ -214,3 +214,34 @@ def test_flat_buffer_layout_matches_arrays():
         assert [tuple(buf[o + 4 * k:o + 4 * k + 4]) for k in range(ni)] == [tuple(r) for r in st["items"]]
         o = buf[at + 10]
         assert buf[o:o + W + 1] == st["wip"]
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_item_meta_describes_each_items_request_and_row(seed):
+    """item_meta restates, per item, what the row and the inputs say about its
+    request; checked here from the raw index arrays, item by item."""
+    rng = np.random.default_rng(500 + seed)
+    P = int(rng.choice([1, 16]))
+    B = int(rng.integers(1, 12))
+    qo = rng.integers(0, 40, size=B)
+    kv = np.array([rng.integers(max(int(q), 1) if q >= 2 else 0, 300) for q in qo])
+    npg = -(-kv // P)
+    kv_indptr = np.concatenate([[0], np.cumsum(npg)]).astype(np.int32)
+    last = np.where(npg > 0, kv - (npg - 1) * P, 1).astype(np.int32)
+    for qo_indptr in (None, np.concatenate([[0], np.cumsum(qo)]).astype(np.int32)):
+        code, res = pr.plan(qo_indptr, kv_indptr, last, page_size=P, num_qo_heads=8, num_kv_heads=2,
+                            head_dim=64, causal=True, workers_decode=5, workers_prefill=3,
+                            min_seg_pages=1)
+        assert code == 0, res
+        for name in ("decode", "prefill"):
+            st = res[name]
+            assert len(st["item_meta"]) == len(st["items"])
+            for (r, pb, pe, slot), m in zip(st["items"], st["item_meta"]):
+                req, rb, re, _ = st["rows"][r]
+                n_pages = kv_indptr[req + 1] - kv_indptr[req]
+                want_kv = 0 if n_pages == 0 else (n_pages - 1) * P + last[req]
+                want_qb = req if qo_indptr is None else qo_indptr[req]
+                want_ql = 1 if qo_indptr is None else qo_indptr[req + 1] - qo_indptr[req]
+                assert m == (req, kv_indptr[req], want_kv, want_qb, want_ql, rb, re, 0)
+            off = st["off_item_meta"]
+            assert res["buf"][off:off + 8 * len(st["item_meta"])] == [x for m in st["item_meta"] for x in m]
