@@ -63,6 +63,15 @@ __device__ __forceinline__ uint32_t pack_f16_rtz(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
 }
 
+// max of three floats as one v_max3_f32.  Written out so that the compiler
+// does not quieten each input first: the logits it is applied to are finite
+// or -inf (masked), never NaN.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // v_permlane32_swap on (x, x) leaves x of lane l % 32 in one result and x of
 // lane l % 32 + 32 in the other, in every lane: combining the two gives the
 // pair's max / sum in both halves.
@@ -159,6 +168,7 @@ void prefill_kernel(PrefillParams a) {
   const int tok_bytes = Hk * D * 2;
   const int64_t half_bytes = (int64_t)P * tok_bytes;
   const int64_t page_bytes = 2 * half_bytes;
+  const uint32_t page_bytes_u = (uint32_t)page_bytes;  // < 2^32: checked on the host
   const uint8_t* kv_head = a.kv + (int64_t)g * D * 2;
   // staging roles.  K: load j of wave w fills tile bytes (w KDma + j) 1024 +
   // 16 lane, i.e. key k_key(j) (the wave's keys are 16 consecutive ones),
@@ -234,6 +244,8 @@ void prefill_kernel(PrefillParams a) {
     // later, so the load is never waited for early; an id outside the pool
     // reads page 0 instead
     auto checked = [&](int pg) -> uint32_t { return (uint32_t)pg < pool_lim ? (uint32_t)pg : 0u; };
+    const int32_t* kvi = a.kv_indices + kvb;  // this request's page ids (uniform base)
+    auto raw_page = [&](int key) -> int { return kvi[(uint32_t)page_idx(key)]; };
     // With power-of-two pages of >= 16 tokens (FAST) a wave's 16 K keys sit
     // in one page (tiles start on 16-key boundaries), whose id is then
     // wave-uniform, and so do a thread's 4 V keys.  K keys past t1 need no
@@ -251,10 +263,10 @@ void prefill_kernel(PrefillParams a) {
       const int ts = t0 + n * kTileK;
       if constexpr (FAST) {
         const int pi = min(page_idx(ts + wave_u * SH::KeysPerWave), page_idx(t1 - 1));
-        pg.id[0] = n < ntiles ? a.kv_indices[kvb + pi] : 0;  // same in every lane of the wave
+        pg.id[0] = n < ntiles ? kvi[(uint32_t)pi] : 0;  // same in every lane of the wave
       } else {
 #pragma unroll
-        for (int j = 0; j < SH::KDma; ++j) pg.id[j] = n < ntiles ? a.kv_indices[kvb + page_idx(clamp_key(ts + k_key(j)))] : 0;
+        for (int j = 0; j < SH::KDma; ++j) pg.id[j] = n < ntiles ? raw_page(clamp_key(ts + k_key(j))) : 0;
       }
       return pg;
     };
@@ -263,10 +275,10 @@ void prefill_kernel(PrefillParams a) {
       const int ts = t0 + n * kTileK;
       const bool ok = n < ntiles && v_active;
       if constexpr (FAST) {
-        pg.id[0] = ok ? a.kv_indices[kvb + page_idx(clamp_key(ts + 4 * v_kg))] : 0;
+        pg.id[0] = ok ? raw_page(clamp_key(ts + 4 * v_kg)) : 0;
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pg.id[j] = ok ? a.kv_indices[kvb + page_idx(clamp_key(ts + 4 * v_kg + j))] : 0;
+        for (int j = 0; j < 4; ++j) pg.id[j] = ok ? raw_page(clamp_key(ts + 4 * v_kg + j)) : 0;
       }
       return pg;
     };
@@ -297,11 +309,18 @@ void prefill_kernel(PrefillParams a) {
       if (v_active) {
         const int ts = t0 + n * kTileK;
         const uint8_t* base = kv_head + half_bytes + v_piece * 16;
+        if (FAST && ts + kTileK <= t1) {  // whole tile valid: the 4 keys are consecutive slots of one page
+          const uint8_t* b0 = base + (uint64_t)checked(pg.id[0]) * page_bytes_u +
+                              __umul24((uint32_t)slot_of(ts + 4 * v_kg), (uint32_t)tok_bytes);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int kc = clamp_key(ts + 4 * v_kg + j);
-          const uint8_t* pbase = base + (int64_t)checked(pg.id[FAST ? 0 : j]) * page_bytes;
-          vreg[j] = load16(pbase + __umul24(slot_of(kc), tok_bytes));
+          for (int j = 0; j < 4; ++j) vreg[j] = load16(b0 + (uint32_t)(j * tok_bytes));
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int kc = clamp_key(ts + 4 * v_kg + j);
+            const uint8_t* pbase = base + (uint64_t)checked(pg.id[FAST ? 0 : j]) * page_bytes_u;
+            vreg[j] = load16(pbase + __umul24((uint32_t)slot_of(kc), (uint32_t)tok_bytes));
+          }
         }
       }
     };
@@ -372,21 +391,32 @@ void prefill_kernel(PrefillParams a) {
         for (int e = 0; e < 16; ++e) s[e] = 8 * (e >> 2) + (e & 3) < rel ? s[e] : neg_inf();
       }
     };
-    // online softmax of a prepared block: P^T (fp16) for its 2 PV k-steps;
-    // returns the factor the accumulator must be rescaled by
-    auto softmax = [&](f32x16_t& s, f16x8_t (&pb)[2]) -> float {
-      float tm = fmaxf(fmaxf(s[0], s[1]), s[2]);
+    // Online softmax of a prepared block, in two parts.  update_max: the
+    // block's row max; the running max moves only when a block beats it by
+    // more than 2^8, and then (rarely, wave-uniform branch) the accumulator
+    // and the row sum are rescaled.  exps: P^T (fp16) for the block's 2 PV
+    // k-steps, its row sum (over the packed values) added into l_part.
+    float m_use = 0.f;  // m_run, or 0 while it is -inf
+    auto update_max = [&](f32x16_t& s) {
+      float tm = max3(s[0], s[1], s[2]);
 #pragma unroll
-      for (int e = 3; e < 15; e += 2) tm = fmaxf(fmaxf(tm, s[e]), s[e + 1]);
+      for (int e = 3; e < 15; e += 2) tm = max3(tm, s[e], s[e + 1]);
       tm = fmaxf(tm, s[15]);
       const float tmax = half_max(tm) * sc;
-      // the reference max only moves when a block beats it by more than 2^8
-      const float m_new = tmax > m_run + kMaxSlack ? tmax : m_run;
-      const float m_use = m_new == neg_inf() ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      m_run = m_new;
+      const bool move = tmax > m_run + kMaxSlack;
+      if (__builtin_expect(__any(move), 0)) {
+        const float m_new = move ? tmax : m_run;
+        const float m_new_use = m_new == neg_inf() ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - m_new_use);  // 1 where the max stays, 0 from -inf
+#pragma unroll
+        for (int d = 0; d < SH::DBlocks; ++d) oacc[d] *= alpha;
+        l_part *= alpha;
+        m_run = m_new;
+        m_use = m_new_use;
+      }
+    };
+    auto exps = [&](const f32x16_t& s, f16x8_t (&pb)[2]) {
       const f16x2_t ones = {(_Float16)1.f, (_Float16)1.f};
-      float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
 #pragma unroll
@@ -396,17 +426,8 @@ void prefill_kernel(PrefillParams a) {
           const f16x2_t pp = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(p0, p1));
           pb[k][2 * i] = pp[0];
           pb[k][2 * i + 1] = pp[1];
-          if (i & 1) ls1 = __builtin_amdgcn_fdot2(pp, ones, ls1, false);
-          else ls0 = __builtin_amdgcn_fdot2(pp, ones, ls0, false);
+          l_part = __builtin_amdgcn_fdot2(pp, ones, l_part, false);
         }
-      }
-      l_part = l_part * alpha + (ls0 + ls1);
-      return alpha;
-    };
-    auto rescale = [&](float alpha) {
-      if (__builtin_expect(__any(alpha != 1.f), 0)) {  // wave-uniform; rare once the max settles
-#pragma unroll
-        for (int d = 0; d < SH::DBlocks; ++d) oacc[d] *= alpha;
       }
     };
 
@@ -429,11 +450,6 @@ void prefill_kernel(PrefillParams a) {
     if (ntiles > 0) store_v(v_lds0);
     FI_WAIT_VMCNT(0);
     __syncthreads();
-    // fences: P must be materialised before the (rare) rescale branch, so
-    // the exponentials stay next to the products they overlap with
-    auto fence = [](const f16x8_t (&pb)[2]) {
-      asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, pb[0])), "v"(__builtin_bit_cast(u32x4_t, pb[1])));
-    };
     // Loads for tile n + 1 are issued even past the last tile (page ids of
     // tiles past the end read as 0, a valid page): nothing reads that data,
     // and the body stays free of branches.
@@ -457,17 +473,15 @@ void prefill_kernel(PrefillParams a) {
       prepare(n, 0, s0, mask_tag);
       // QK(b1) + softmax(b0) + V(b0) reads
       qk(kop1, s1);
+      update_max(s0);
       vread(vb, 0, vop0);
-      const float a0 = softmax(s0, p0);
-      fence(p0);
-      rescale(a0);
+      exps(s0, p0);
       prepare(n, 1, s1, mask_tag);
       // PV(b0) + softmax(b1) + V(b1) reads
       pv(vop0, p0);
+      update_max(s1);
       vread(vb, 1, vop1);
-      const float a1 = softmax(s1, p1);
-      fence(p1);
-      rescale(a1);
+      exps(s1, p1);
       // PV(b1) + the conversion of the next V tile
       pv(vop1, p1);
       store_v(vb_next);
@@ -562,6 +576,8 @@ int launch_d(const RunArgs& r, const PrefillParams& p) {
 int launch_prefill(const RunArgs& r) {
   if (r.dtype != FI_BF16)
     return set_error(FI_ERR_UNSUPPORTED, "prefill tiles need bf16 q / kv (fp32 runs decode rows only)");
+  if ((int64_t)4 * r.P * r.Hk * r.D >= ((int64_t)1 << 32))
+    return set_error(FI_ERR_UNSUPPORTED, "prefill: one page of the pool must stay below 4 GiB");
   PrefillParams p;
   p.plan = r.plan;
   p.q = static_cast<const uint8_t*>(r.q);
