@@ -417,23 +417,92 @@ void decode_mfma_kernel(DecodeParams a) {
   const int tr_tok = 4 * kq + (tk >> 2);
   const int tr_sub = tk & 3;
 
-  float* acc_lds = reinterpret_cast<float*>(&vring[0][0][0]);  // epilogue reuse: [kWaves][G][D]
-  static_assert(sizeof(float) * kWaves * G * D <= sizeof(vring), "epilogue scratch");
+  // epilogue scratch of its own: the V ring is already loading the next item
+  __shared__ __align__(16) float acc_lds[kWaves * G * D];
 
   const int it_begin = wip[worker];
   const int it_end = wip[worker + 1];
+  // An item's record is loaded while the previous item runs, so only the
+  // first item of a worker waits for it.
+  struct Rec {
+    int pb, pe, slot, kvb, kv_len, qrow;
+  };
+  auto load_rec = [&](int it) -> Rec {
+    Rec r{0, 0, -1, 0, 0, 0};
+    if (it < it_end) {
+      const int32_t* im = meta + kMetaInts * it;
+      r = Rec{items[4 * it + 1], items[4 * it + 2], items[4 * it + 3], im[M_KVB], im[M_KVLEN], im[M_QOBASE]};
+    }
+    return r;
+  };
+  // item geometry: keys [t0, t1), chunks of kChunk keys, the request's page ids at kvb
+  struct Ctx {
+    int t0, t1, kvb, nch;
+  };
+  auto make_ctx = [&](const Rec& r) -> Ctx {
+    const int t0 = r.pb * P, t1 = min(r.pe * P, r.kv_len);
+    return Ctx{t0, t1, r.kvb, t1 > t0 ? (t1 - t0 + kChunk - 1) / kChunk : 0};
+  };
+  // page id of the wave's chunk 64 batch + lane, loaded raw (checked where
+  // it is read, so the load is not waited for on the spot)
+  auto load_pids = [&](const Ctx& x, int batch) -> int {
+    const int c = wave + kWaves * (64 * batch + lane);
+    return c < x.nch ? a.kv_indices[x.kvb + ((x.t0 + c * kChunk) >> a.page_shift)] : 0;
+  };
+  // K -> registers, V -> LDS stage `st` for the wave's kth chunk c
+  auto issue = [&](const Ctx& x, int pid_vec, int c, int kth, int st, u32x4_t (&kb)[NK]) {
+    const int cs = x.t0 + c * kChunk;
+    const int pid = __builtin_amdgcn_readlane(pid_vec, kth & 63);
+    const int64_t page = (uint32_t)pid < (uint64_t)a.pool_pages ? pid : 0;  // never read outside the pool
+    const int slot0 = cs & (P - 1);
+    const int last = x.t1 - 1 - cs;  // last valid token of the chunk (may exceed 15)
+    const uint8_t* pbase = a.kv + (page * page_stride + (int64_t)g * D) * 2;
+    const uint8_t* kaddr = pbase + (int64_t)(slot0 + min(tk, last)) * tok_stride * 2;
+#pragma unroll
+    for (int p = 0; p < NK; ++p) kb[p] = load16(kaddr + (4 * p + kq) * 16);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int t = (k * 1024 + 16 * lane) / RB;
+      const int pp = ((16 * lane) % RB) / 16;
+      const int piece = pp ^ (t & (NP - 1));
+      const uint8_t* src = pbase + (half_stride + (int64_t)(slot0 + min(t, last)) * tok_stride) * 2 + piece * 16;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                       (FI_LDS void*)(&vring[wave][st][k * 1024]), 16, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // max / sum over the 4 lanes that hold one head (l, l ^ 16, l ^ 32, l ^ 48)
+  auto head_max = [](float v) {
+    auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+    auto pq = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(pq[0]), __uint_as_float(pq[1]));
+  };
+  auto head_sum = [](float v) {
+    auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+    auto pq = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(pq[0]) + __uint_as_float(pq[1]);
+  };
+
+  // The first chunk of the next item is issued when the current item's
+  // chunks are done, before its epilogue, and that item's page ids are
+  // fetched during the current one: consecutive items of a worker overlap.
+  u32x4_t kA[NK], kB[NK];
+  Rec nxt = load_rec(it_begin);
+  bool pre_issued = false;  // chunk 0 of the coming item is in kA / stage 0
+  int pid_pre = 0;          // page ids (batch 0) of the coming item, when pre_issued
   for (int it = it_begin; it < it_end; ++it) {
-    // the item and its request's record: two independent loads
-    const int pb = items[4 * it + 1];
-    const int pe = items[4 * it + 2];
-    const int slot = items[4 * it + 3];
-    const int32_t* im = meta + kMetaInts * it;
-    const int kvb = im[M_KVB];
-    const int kv_len = im[M_KVLEN];
-    const int t0 = pb * P;
-    const int t1 = min(pe * P, kv_len);
-    const int qrow = im[M_QOBASE];
-    const int nch = t1 > t0 ? (t1 - t0 + kChunk - 1) / kChunk : 0;
+    const Rec cur = nxt;
+    nxt = load_rec(it + 1);
+    const Ctx cx = make_ctx(cur);
+    const int slot = cur.slot;
+    const int t0 = cx.t0, t1 = cx.t1;
+    const int qrow = cur.qrow;
+    const int nch = cx.nch;
+    const int myn = nch > wave ? (nch - wave + kWaves - 1) / kWaves : 0;
+    int pid_vec = pre_issued ? pid_pre : load_pids(cx, 0);
 
     u32x4_t qp[NK];
     {
@@ -450,34 +519,9 @@ void decode_mfma_kernel(DecodeParams a) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) oacc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    int pid_vec = 0;
-    auto load_pids = [&](int batch) {
-      const int c = wave + kWaves * (64 * batch + lane);
-      int pg = c < nch ? a.kv_indices[kvb + ((t0 + c * kChunk) >> a.page_shift)] : 0;
-      pid_vec = (uint32_t)pg < (uint64_t)a.pool_pages ? pg : 0;  // never read outside the pool
-    };
-    // K -> registers, V -> LDS stage `st` for the wave's kth chunk c
-    auto issue = [&](int c, int kth, int st, u32x4_t (&kb)[NK]) {
-      if ((kth & 63) == 0) load_pids(kth >> 6);
-      const int cs = t0 + c * kChunk;
-      const int64_t page = __builtin_amdgcn_readlane(pid_vec, kth & 63);
-      const int slot0 = cs & (P - 1);
-      const int last = t1 - 1 - cs;  // last valid token of the chunk (may exceed 15)
-      const uint8_t* pbase = a.kv + (page * page_stride + (int64_t)g * D) * 2;
-      const uint8_t* kaddr = pbase + (int64_t)(slot0 + min(tk, last)) * tok_stride * 2;
-#pragma unroll
-      for (int p = 0; p < NK; ++p) kb[p] = load16(kaddr + (4 * p + kq) * 16);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int k = 0; k < NV; ++k) {
-        const int t = (k * 1024 + 16 * lane) / RB;
-        const int pp = ((16 * lane) % RB) / 16;
-        const int piece = pp ^ (t & (NP - 1));
-        const uint8_t* src = pbase + (half_stride + (int64_t)(slot0 + min(t, last)) * tok_stride) * 2 + piece * 16;
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
-                                         (FI_LDS void*)(&vring[wave][st][k * 1024]), 16, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    auto issue_k = [&](int c, int kth, int st, u32x4_t (&kb)[NK]) {
+      if ((kth & 63) == 0 && kth > 0) pid_vec = load_pids(cx, kth >> 6);
+      issue(cx, pid_vec, c, kth, st, kb);
     };
 
     auto compute = [&](int c, int st, const u32x4_t (&kb)[NK]) {
@@ -496,9 +540,7 @@ void decode_mfma_kernel(DecodeParams a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) x[r] = (cs + 4 * kq + r < t1) ? x[r] : neg_inf();
       }
-      float cm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      cm = fmaxf(cm, __shfl_xor(cm, 16));
-      cm = fmaxf(cm, __shfl_xor(cm, 32));
+      const float cm = head_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
       const float m_new = cm > m_run + kMaxSlack ? cm : m_run;
       const float m_use = m_new == neg_inf() ? 0.f : m_new;
       const float alpha = fast_exp2(m_run - m_use);
@@ -529,31 +571,46 @@ void decode_mfma_kernel(DecodeParams a) {
       }
     };
 
+    const bool has_next = it + 1 < it_end;
+    Ctx nx{0, 0, 0, 0};
+    int pid_next = 0;
     {
-      u32x4_t kA[NK], kB[NK];
-      const int myn = nch > wave ? (nch - wave + kWaves - 1) / kWaves : 0;
-      if (myn > 0) issue(wave, 0, 0, kA);
+      if (myn > 0 && !pre_issued) issue_k(wave, 0, 0, kA);
       for (int k = 0; k < myn; k += 2) {
         const bool n1 = k + 1 < myn;
-        if (n1) issue(wave + kWaves * (k + 1), k + 1, 1, kB);
+        if (n1) issue_k(wave + kWaves * (k + 1), k + 1, 1, kB);
         if (n1) FI_WAIT_VMCNT(2 * NK); else FI_WAIT_VMCNT(0);
         __builtin_amdgcn_sched_barrier(0);
         compute(wave + kWaves * k, 0, kA);
         __builtin_amdgcn_sched_barrier(0);
+        if (k == 0 && has_next) {  // the next item's record has landed by now
+          nx = make_ctx(nxt);
+          pid_next = load_pids(nx, 0);
+        }
         if (!n1) break;
         const bool n2 = k + 2 < myn;
-        if (n2) issue(wave + kWaves * (k + 2), k + 2, 0, kA);
+        if (n2) issue_k(wave + kWaves * (k + 2), k + 2, 0, kA);
         if (n2) FI_WAIT_VMCNT(2 * NK); else FI_WAIT_VMCNT(0);
         __builtin_amdgcn_sched_barrier(0);
         compute(wave + kWaves * (k + 1), 1, kB);
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (myn == 0 && has_next) {
+        nx = make_ctx(nxt);
+        pid_next = load_pids(nx, 0);
+      }
+      // chunk 0 of the next item, into kA / stage 0 (this wave's last chunk
+      // has been computed, so both are free)
+      pre_issued = has_next && nx.nch > wave;
+      if (pre_issued) {
+        pid_pre = pid_next;
+        issue(nx, pid_pre, wave, 0, 0, kA);
+      }
     }
 
-    // wave totals, then merge the four waves through LDS
-    l_part += __shfl_xor(l_part, 16);
-    l_part += __shfl_xor(l_part, 32);
-    __syncthreads();  // every wave is done with its V ring before it turns into scratch
+    // wave totals (sum over the 4 lanes of a head: l, l ^ 16, l ^ 32, l ^ 48),
+    // then merge the four waves through LDS
+    l_part = head_sum(l_part);
     if (lane < G) {
       m_lds[wave][lane] = m_run;
       l_lds[wave][lane] = l_part;
@@ -561,8 +618,7 @@ void decode_mfma_kernel(DecodeParams a) {
     if (hS < G) {
 #pragma unroll
       for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc_lds[(wave * G + hS) * D + 16 * b + 4 * kq + r] = oacc[b][r];
+        *reinterpret_cast<f32x4_t*>(&acc_lds[(wave * G + hS) * D + 16 * b + 4 * kq]) = oacc[b];
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
