@@ -109,7 +109,7 @@ def run_decode_bench(args):
                           workers_prefill=1, min_seg_pages=args.min_seg_pages,
                           out=pinned[j].numpy())
         info["plan"] = plan
-        plan_dev[j][: plan.ints].copy_(pinned[j][: plan.ints], non_blocking=True)
+        plan_dev[j].copy_(pinned[j], non_blocking=True)  # whole buffer: no per-step slicing
         copied[j].record()
         if timed_idx is not None:
             starts[timed_idx].record()

@@ -50,9 +50,9 @@ class FIError(RuntimeError):
 
 class fi_plan_in(ctypes.Structure):
     _fields_ = [("batch_size", ctypes.c_int32),
-                ("qo_indptr", ctypes.POINTER(ctypes.c_int32)),
-                ("kv_indptr", ctypes.POINTER(ctypes.c_int32)),
-                ("kv_last_page_len", ctypes.POINTER(ctypes.c_int32)),
+                ("qo_indptr", ctypes.c_void_p),         # const int32_t*
+                ("kv_indptr", ctypes.c_void_p),         # const int32_t*
+                ("kv_last_page_len", ctypes.c_void_p),  # const int32_t*
                 ("page_size", ctypes.c_int32),
                 ("num_qo_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32),
@@ -97,7 +97,7 @@ def lib():
             raise FIError(FI_ERR_HIP, f"{LIB_PATH} is not built; run paged_kv_block_bsr_amd/build.py")
         L = ctypes.CDLL(LIB_PATH)
         vp, i32p, i64p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
-        L.fi_plan.argtypes = [ctypes.POINTER(fi_plan_in), i32p, ctypes.c_int64,
+        L.fi_plan.argtypes = [ctypes.POINTER(fi_plan_in), vp, ctypes.c_int64,
                               ctypes.POINTER(fi_plan_info)]
         L.fi_plan_bounds.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, i64p, i64p]
@@ -130,6 +130,8 @@ def _check(rc: int):
 def _i32_host(a) -> Optional[np.ndarray]:
     if a is None:
         return None
+    if type(a) is np.ndarray and a.dtype == np.int32 and a.flags.c_contiguous:
+        return a
     if isinstance(a, torch.Tensor):
         a = a.detach().cpu().numpy()
     return np.ascontiguousarray(np.asarray(a), dtype=np.int32)
@@ -198,6 +200,8 @@ def fi_plan(qo_indptr, kv_indptr, kv_last_page_len, *, page_size, num_qo_heads, 
     if kl is None or len(kl) == 0:
         kl = np.zeros(max(B, 1), np.int32)
     total_qo = B if qo is None else int(qo[-1])
+    if capacity is None and out is not None:
+        capacity = len(out)  # fi_plan itself rejects a buffer that is too small
     if capacity is None:
         ints = ctypes.c_int64()
         _check(lib().fi_plan_bounds(B, total_qo, num_qo_heads, num_kv_heads, head_dim,
@@ -205,14 +209,11 @@ def fi_plan(qo_indptr, kv_indptr, kv_last_page_len, *, page_size, num_qo_heads, 
                                     ctypes.byref(ints), None))
         capacity = int(ints.value)
     buf = out if out is not None else np.zeros(capacity, np.int32)
-    i32p = ctypes.POINTER(ctypes.c_int32)
-    pin = fi_plan_in(B,
-                     qo.ctypes.data_as(i32p) if qo is not None else None,
-                     kp.ctypes.data_as(i32p), kl.ctypes.data_as(i32p),
+    pin = fi_plan_in(B, qo.ctypes.data if qo is not None else None, kp.ctypes.data, kl.ctypes.data,
                      page_size, num_qo_heads, num_kv_heads, head_dim, int(bool(causal)),
                      workers_decode, workers_prefill, min_seg_pages, br_override, no_split)
     info = fi_plan_info()
-    _check(lib().fi_plan(ctypes.byref(pin), buf.ctypes.data_as(i32p), len(buf), ctypes.byref(info)))
+    _check(lib().fi_plan(ctypes.byref(pin), buf.ctypes.data, len(buf), ctypes.byref(info)))
     return Plan(buf=buf, info=info)
 
 

@@ -193,41 +193,195 @@ void prefill_kernel(PrefillParams a) {
 
   const int it_begin = wip[worker];
   const int it_end = wip[worker + 1];
+
+  // ---- items.  An item's record and the page ids of its first tile are
+  // loaded early in the item before it, its query rows and first K/V tile
+  // before that item's epilogue: consecutive items of a worker overlap
+  // instead of paying three dependent memory round trips each.
+  struct Item {
+    int pb, pe, slot, rb, re, kvb, kv_len, qbase, qo_len;
+  };
+  auto load_item = [&](int it) -> Item {
+    Item x{0, 0, -1, 0, 0, 0, 0, 0, 0};  // past the worker's last item: no keys
+    if (it < it_end) {
+      const int32_t* im = meta + kMetaInts * it;
+      x = Item{items[4 * it + 1], items[4 * it + 2], items[4 * it + 3], im[M_RB], im[M_RE],
+               im[M_KVB],         im[M_KVLEN],       im[M_QOBASE],      im[M_QOLEN]};
+    }
+    return x;
+  };
+  // the fields are wave-uniform: scalar registers hold them across an item
+  // (converted once the loads are known to have landed, so that the
+  // conversion does not wait for them)
+  auto uniform = [](const Item& x) {
+    auto u = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+    return Item{u(x.pb), u(x.pe), u(x.slot), u(x.rb), u(x.re), u(x.kvb), u(x.kv_len), u(x.qbase), u(x.qo_len)};
+  };
+  // an item's keys [t0, t1) in ntiles tiles, and its request's page ids
+  struct Ctx {
+    int t0, t1, ntiles;
+    const int32_t* kvi;
+  };
+  auto make_ctx = [&](const Item& x) -> Ctx {
+    const int t0 = x.pb * P, t1 = min(x.pe * P, x.kv_len);
+    return Ctx{t0, t1, t1 > t0 ? (t1 - t0 + kTileK - 1) / kTileK : 0, a.kv_indices + x.kvb};
+  };
+  // this lane's packed row of an item, and that row's token and head
+  auto row_of = [&](const Item& x) { return x.rb + kRowsPerWave * wave + l32; };
+  auto tok_head = [&](const Item& x, int& tok, int& head) {
+    const int r = row_of(x);
+    const int rc = r < x.re ? r : x.re - 1;
+    tok = rc / G;
+    head = g * G + rc % G;
+  };
+
+  // ---- staging
+  auto page_idx = [&](int key) { return FAST ? key >> a.page_shift : key / P; };
+  auto slot_of = [&](int key) { return FAST ? key & (P - 1) : key % P; };
+  auto clamp_key = [&](const Ctx& c, int key) { return key < c.t1 ? key : c.t1 - 1; };
+  // page ids are loaded raw and checked where they are used, a tile
+  // later, so the load is never waited for early; an id outside the pool
+  // reads page 0 instead
+  auto checked = [&](int pg) -> uint32_t { return (uint32_t)pg < pool_lim ? (uint32_t)pg : 0u; };
+  auto raw_page = [&](const Ctx& c, int key) -> int { return c.kvi[(uint32_t)page_idx(key)]; };
+  // With power-of-two pages of >= 16 tokens (FAST) a wave's 16 K keys sit
+  // in one page (tiles start on 16-key boundaries), whose id is then
+  // wave-uniform, and so do a thread's 4 V keys.  K keys past t1 need no
+  // clamping beyond the page (their logits are masked; the page is
+  // valid); V keys are clamped to t1 - 1 so that masked keys still read
+  // finite values (P = 0 times a NaN would not vanish).
+  struct KPages {
+    int id[FAST ? 1 : SH::KDma];
+  };
+  struct VPages {
+    int id[FAST ? 1 : 4];
+  };
+  auto fetch_k = [&](const Ctx& c, int n) -> KPages {
+    KPages pg;
+    const int ts = c.t0 + n * kTileK;
+    if constexpr (FAST) {
+      const int pi = min(page_idx(ts + wave_u * SH::KeysPerWave), page_idx(c.t1 - 1));
+      pg.id[0] = n < c.ntiles ? c.kvi[(uint32_t)pi] : 0;  // same in every lane of the wave
+    } else {
+#pragma unroll
+      for (int j = 0; j < SH::KDma; ++j) pg.id[j] = n < c.ntiles ? raw_page(c, clamp_key(c, ts + k_key(j))) : 0;
+    }
+    return pg;
+  };
+  auto fetch_v = [&](const Ctx& c, int n) -> VPages {
+    VPages pg;
+    const int ts = c.t0 + n * kTileK;
+    const bool ok = n < c.ntiles && v_active;
+    if constexpr (FAST) {
+      pg.id[0] = ok ? raw_page(c, clamp_key(c, ts + 4 * v_kg)) : 0;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pg.id[j] = ok ? raw_page(c, clamp_key(c, ts + 4 * v_kg + j)) : 0;
+    }
+    return pg;
+  };
+  auto dma_k = [&](const Ctx& c, int n, uint8_t* kb, const KPages& pg) {
+    const int ts = c.t0 + n * kTileK;
+    if constexpr (FAST) {
+      const int pid = __builtin_amdgcn_readfirstlane(pg.id[0]);
+      const uint8_t* base = kv_head + (int64_t)checked(pid) * page_bytes +
+                            slot_of(ts + wave_u * SH::KeysPerWave) * tok_bytes;
+#pragma unroll
+      for (int j = 0; j < SH::KDma; ++j)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + k_off[j]),
+                                         (FI_LDS void*)(kb + (wave_u * SH::KDma + j) * 1024), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < SH::KDma; ++j) {
+        const int key = k_key(j);
+        const int kc = clamp_key(c, ts + key);
+        const uint8_t* src = kv_head + (int64_t)checked(pg.id[j]) * page_bytes +
+                             (uint32_t)(slot_of(kc) * tok_bytes + (k_pp ^ (key & (SH::KPiecesRow - 1))) * 16);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                         (FI_LDS void*)(kb + (wave_u * SH::KDma + j) * 1024), 16, 0, 0);
+      }
+    }
+  };
+  u32x4_t vreg[4] = {};
+  auto load_v = [&](const Ctx& c, int n, const VPages& pg) {
+    if (v_active) {
+      const int ts = c.t0 + n * kTileK;
+      const uint8_t* base = kv_head + half_bytes + v_piece * 16;
+      if (FAST && ts + kTileK <= c.t1) {  // whole tile valid: the 4 keys are consecutive slots of one page
+        const uint8_t* b0 = base + (uint64_t)checked(pg.id[0]) * page_bytes_u +
+                            __umul24((uint32_t)slot_of(ts + 4 * v_kg), (uint32_t)tok_bytes);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vreg[j] = load16(b0 + (uint32_t)(j * tok_bytes));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int kc = clamp_key(c, ts + 4 * v_kg + j);
+          const uint8_t* pbase = base + (uint64_t)checked(pg.id[FAST ? 0 : j]) * page_bytes_u;
+          vreg[j] = load16(pbase + __umul24((uint32_t)slot_of(kc), (uint32_t)tok_bytes));
+        }
+      }
+    }
+  };
+  auto store_v = [&](uint16_t* vb) {
+    if (v_active) {
+      uint16_t* dst = vb + (8 * v_piece) * kVStride + vt_pos(4 * v_kg);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        u32x2_t lo, hi;  // dims 2w and 2w + 1 of the piece, keys 4 kg .. + 3
+        lo[0] = pack_f16_rtz(bf16_lo(vreg[0][w]), bf16_lo(vreg[1][w]));
+        lo[1] = pack_f16_rtz(bf16_lo(vreg[2][w]), bf16_lo(vreg[3][w]));
+        hi[0] = pack_f16_rtz(bf16_hi(vreg[0][w]), bf16_hi(vreg[1][w]));
+        hi[1] = pack_f16_rtz(bf16_hi(vreg[2][w]), bf16_hi(vreg[3][w]));
+        *reinterpret_cast<u32x2_t*>(dst + (2 * w) * kVStride) = lo;
+        *reinterpret_cast<u32x2_t*>(dst + (2 * w + 1) * kVStride) = hi;
+      }
+    }
+  };
+
+  // packed query rows as the MFMA B operand (dims 16 ks + 8 hh .. + 8)
+  bf16x8_t qp[SH::KSteps];
+  auto load_q = [&](const Item& x) {
+    int tok, head;
+    tok_head(x, tok, head);
+    const uint8_t* qb = a.q + ((int64_t)(x.qbase + tok) * a.Hq + head) * D * 2;
+#pragma unroll
+    for (int ks = 0; ks < SH::KSteps; ++ks)
+      qp[ks] = __builtin_bit_cast(bf16x8_t, load16(qb + (16 * ks + 8 * hh) * 2));
+  };
+
+  // the worker's first item: query rows, tile 0 and the page ids of tile 1
+  Item item = uniform(load_item(it_begin));
+  KPages pk{};
+  VPages pv_ids{};
+  if (it_begin < it_end) {
+    const Ctx c = make_ctx(item);
+    load_q(item);
+    pk = fetch_k(c, 0);
+    pv_ids = fetch_v(c, 0);
+    if (c.ntiles > 0) {
+      dma_k(c, 0, k_lds0, pk);
+      load_v(c, 0, pv_ids);
+    }
+    pk = fetch_k(c, 1);
+    pv_ids = fetch_v(c, 1);
+  }
+
   for (int it = it_begin; it < it_end; ++it) {
-    // the item and its request's record: two independent loads
-    const int pb = items[4 * it + 1];
-    const int pe = items[4 * it + 2];
-    const int slot = items[4 * it + 3];
-    const int32_t* im = meta + kMetaInts * it;
-    const int rb = im[M_RB];
-    const int re = im[M_RE];
-    const int kvb = im[M_KVB];
-    const int kv_len = im[M_KVLEN];
-    const int qbase = im[M_QOBASE];
-    const int qo_len = im[M_QOLEN];
-    const int t0 = pb * P;
-    const int t1 = min(pe * P, kv_len);
-    const int ntiles = t1 > t0 ? (t1 - t0 + kTileK - 1) / kTileK : 0;
+    const Item nxt_raw = load_item(it + 1);
+    const Ctx cx = make_ctx(item);
+    const int t0 = cx.t0, ntiles = cx.ntiles;
+    const int slot = item.slot, rb = item.rb, re = item.re, qbase = item.qbase;
 
     // this lane's packed row, its token, head and key limit
-    const int r = rb + kRowsPerWave * wave + l32;
+    const int r = row_of(item);
     const bool row_valid = r < re;
-    const int rc = row_valid ? r : re - 1;
-    const int tok = rc / G;
-    const int head = g * G + rc % G;
-    const int causal_off = kv_len - qo_len;
-    const int lim = min(a.causal ? causal_off + tok + 1 : kv_len, t1);
+    int tok, head;
+    tok_head(item, tok, head);
+    const int causal_off = item.kv_len - item.qo_len;
+    const int lim = min(a.causal ? causal_off + tok + 1 : item.kv_len, cx.t1);
     const int r_first = min(rb + kRowsPerWave * wave, re - 1);
-    const int wave_lim_min = min(a.causal ? causal_off + r_first / G + 1 : kv_len, t1);
+    const int wave_lim_min = min(a.causal ? causal_off + r_first / G + 1 : item.kv_len, cx.t1);
 
-    // packed query rows as the MFMA B operand (dims 16 ks + 8 hh .. + 8)
-    bf16x8_t qp[SH::KSteps];
-    {
-      const uint8_t* qb = a.q + ((int64_t)(qbase + tok) * a.Hq + head) * D * 2;
-#pragma unroll
-      for (int ks = 0; ks < SH::KSteps; ++ks)
-        qp[ks] = __builtin_bit_cast(bf16x8_t, load16(qb + (16 * ks + 8 * hh) * 2));
-    }
     f32x16_t oacc[SH::DBlocks];
 #pragma unroll
     for (int d = 0; d < SH::DBlocks; ++d)
@@ -235,110 +389,6 @@ void prefill_kernel(PrefillParams a) {
       for (int e = 0; e < 16; ++e) oacc[d][e] = 0.f;
     float m_run = neg_inf();
     float l_part = 0.f;
-
-    // ---- staging
-    auto page_idx = [&](int key) { return FAST ? key >> a.page_shift : key / P; };
-    auto slot_of = [&](int key) { return FAST ? key & (P - 1) : key % P; };
-    auto clamp_key = [&](int key) { return key < t1 ? key : t1 - 1; };
-    // page ids are loaded raw and checked where they are used, a tile
-    // later, so the load is never waited for early; an id outside the pool
-    // reads page 0 instead
-    auto checked = [&](int pg) -> uint32_t { return (uint32_t)pg < pool_lim ? (uint32_t)pg : 0u; };
-    const int32_t* kvi = a.kv_indices + kvb;  // this request's page ids (uniform base)
-    auto raw_page = [&](int key) -> int { return kvi[(uint32_t)page_idx(key)]; };
-    // With power-of-two pages of >= 16 tokens (FAST) a wave's 16 K keys sit
-    // in one page (tiles start on 16-key boundaries), whose id is then
-    // wave-uniform, and so do a thread's 4 V keys.  K keys past t1 need no
-    // clamping beyond the page (their logits are masked; the page is
-    // valid); V keys are clamped to t1 - 1 so that masked keys still read
-    // finite values (P = 0 times a NaN would not vanish).
-    struct KPages {
-      int id[FAST ? 1 : SH::KDma];
-    };
-    struct VPages {
-      int id[FAST ? 1 : 4];
-    };
-    auto fetch_k = [&](int n) -> KPages {
-      KPages pg;
-      const int ts = t0 + n * kTileK;
-      if constexpr (FAST) {
-        const int pi = min(page_idx(ts + wave_u * SH::KeysPerWave), page_idx(t1 - 1));
-        pg.id[0] = n < ntiles ? kvi[(uint32_t)pi] : 0;  // same in every lane of the wave
-      } else {
-#pragma unroll
-        for (int j = 0; j < SH::KDma; ++j) pg.id[j] = n < ntiles ? raw_page(clamp_key(ts + k_key(j))) : 0;
-      }
-      return pg;
-    };
-    auto fetch_v = [&](int n) -> VPages {
-      VPages pg;
-      const int ts = t0 + n * kTileK;
-      const bool ok = n < ntiles && v_active;
-      if constexpr (FAST) {
-        pg.id[0] = ok ? raw_page(clamp_key(ts + 4 * v_kg)) : 0;
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pg.id[j] = ok ? raw_page(clamp_key(ts + 4 * v_kg + j)) : 0;
-      }
-      return pg;
-    };
-    auto dma_k = [&](int n, uint8_t* kb, const KPages& pg) {
-      const int ts = t0 + n * kTileK;
-      if constexpr (FAST) {
-        const int pid = __builtin_amdgcn_readfirstlane(pg.id[0]);
-        const uint8_t* base = kv_head + (int64_t)checked(pid) * page_bytes +
-                              slot_of(ts + wave_u * SH::KeysPerWave) * tok_bytes;
-#pragma unroll
-        for (int j = 0; j < SH::KDma; ++j)
-          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + k_off[j]),
-                                           (FI_LDS void*)(kb + (wave_u * SH::KDma + j) * 1024), 16, 0, 0);
-      } else {
-#pragma unroll
-        for (int j = 0; j < SH::KDma; ++j) {
-          const int key = k_key(j);
-          const int kc = clamp_key(ts + key);
-          const uint8_t* src = kv_head + (int64_t)checked(pg.id[j]) * page_bytes +
-                               (uint32_t)(slot_of(kc) * tok_bytes + (k_pp ^ (key & (SH::KPiecesRow - 1))) * 16);
-          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
-                                           (FI_LDS void*)(kb + (wave_u * SH::KDma + j) * 1024), 16, 0, 0);
-        }
-      }
-    };
-    u32x4_t vreg[4] = {};
-    auto load_v = [&](int n, const VPages& pg) {
-      if (v_active) {
-        const int ts = t0 + n * kTileK;
-        const uint8_t* base = kv_head + half_bytes + v_piece * 16;
-        if (FAST && ts + kTileK <= t1) {  // whole tile valid: the 4 keys are consecutive slots of one page
-          const uint8_t* b0 = base + (uint64_t)checked(pg.id[0]) * page_bytes_u +
-                              __umul24((uint32_t)slot_of(ts + 4 * v_kg), (uint32_t)tok_bytes);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) vreg[j] = load16(b0 + (uint32_t)(j * tok_bytes));
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int kc = clamp_key(ts + 4 * v_kg + j);
-            const uint8_t* pbase = base + (uint64_t)checked(pg.id[FAST ? 0 : j]) * page_bytes_u;
-            vreg[j] = load16(pbase + __umul24((uint32_t)slot_of(kc), (uint32_t)tok_bytes));
-          }
-        }
-      }
-    };
-    auto store_v = [&](uint16_t* vb) {
-      if (v_active) {
-        uint16_t* dst = vb + (8 * v_piece) * kVStride + vt_pos(4 * v_kg);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          u32x2_t lo, hi;  // dims 2w and 2w + 1 of the piece, keys 4 kg .. + 3
-          lo[0] = pack_f16_rtz(bf16_lo(vreg[0][w]), bf16_lo(vreg[1][w]));
-          lo[1] = pack_f16_rtz(bf16_lo(vreg[2][w]), bf16_lo(vreg[3][w]));
-          hi[0] = pack_f16_rtz(bf16_hi(vreg[0][w]), bf16_hi(vreg[1][w]));
-          hi[1] = pack_f16_rtz(bf16_hi(vreg[2][w]), bf16_hi(vreg[3][w]));
-          *reinterpret_cast<u32x2_t*>(dst + (2 * w) * kVStride) = lo;
-          *reinterpret_cast<u32x2_t*>(dst + (2 * w + 1) * kVStride) = hi;
-        }
-      }
-    };
 
     // ---- compute pieces, per 32-key block b of a tile
     // K operands of block b: key 32 b + l32, dims 16 ks + 8 hh .. + 8
@@ -438,18 +488,23 @@ void prefill_kernel(PrefillParams a) {
     //   conversion of V(n + 1) | one barrier.
     // The compiler does not track direct-to-LDS loads: every thread waits
     // for all of its loads before the barrier.
-    __syncthreads();  // the previous item's last reads of both buffers are done
-    KPages pk = fetch_k(0);
-    VPages pv_ids = fetch_v(0);
-    if (ntiles > 0) {
-      dma_k(0, k_lds0, pk);
-      load_v(0, pv_ids);
-    }
-    pk = fetch_k(1);
-    pv_ids = fetch_v(1);
+    // Tile 0 (K in k_lds0, V in registers), the query rows and the page ids
+    // of tile 1 were issued before the previous item's epilogue (or above).
     if (ntiles > 0) store_v(v_lds0);
     FI_WAIT_VMCNT(0);
     __syncthreads();
+    // the next item's record has landed: the page ids of its first tile
+    // (with pages of any size, 8 ids a lane: fetched after the loop instead,
+    // as holding them through it would spill)
+    const Item nxt = uniform(nxt_raw);
+    const Ctx nc = make_ctx(nxt);
+    KPages npk{};
+    VPages npv{};
+    if constexpr (FAST) {
+      npk = fetch_k(nc, 0);
+      npv = fetch_v(nc, 0);
+    }
+
     // Loads for tile n + 1 are issued even past the last tile (page ids of
     // tiles past the end read as 0, a valid page): nothing reads that data,
     // and the body stays free of branches.
@@ -465,10 +520,10 @@ void prefill_kernel(PrefillParams a) {
       f16x8_t p0[2], p1[2];
       kread(kb, 0, kop0);
       kread(kb, 1, kop1);
-      dma_k(n + 1, kb_next, pk);
-      load_v(n + 1, pv_ids);
-      pk = fetch_k(n + 2);
-      pv_ids = fetch_v(n + 2);
+      dma_k(cx, n + 1, kb_next, pk);
+      load_v(cx, n + 1, pv_ids);
+      pk = fetch_k(cx, n + 2);
+      pv_ids = fetch_v(cx, n + 2);
       qk(kop0, s0);
       prepare(n, 0, s0, mask_tag);
       // QK(b1) + softmax(b0) + V(b0) reads
@@ -495,6 +550,24 @@ void prefill_kernel(PrefillParams a) {
     for (int n = 0; n < ntiles; n += 2) {
       step_any(n, std::false_type{});
       if (n + 1 < ntiles) step_any(n + 1, std::true_type{});
+    }
+
+
+    // The next item's first tile, query rows and tile-1 page ids: every
+    // buffer is free after the last step's barrier (or the one above), and
+    // the epilogue below uses registers only.
+    if (it + 1 < it_end) {
+      load_q(nxt);
+      if constexpr (!FAST) {
+        npk = fetch_k(nc, 0);
+        npv = fetch_v(nc, 0);
+      }
+      if (nc.ntiles > 0) {
+        dma_k(nc, 0, k_lds0, npk);
+        load_v(nc, 0, npv);
+      }
+      pk = fetch_k(nc, 1);
+      pv_ids = fetch_v(nc, 1);
     }
 
     // ---- epilogue: normalise and write this lane's row (dims 32 d + 8 i + 4 hh + j)
@@ -534,6 +607,7 @@ void prefill_kernel(PrefillParams a) {
         if (hh == 0) ws_lse[prow] = lse_nat;
       }
     }
+    item = nxt;
   }
 }
 
