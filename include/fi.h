@@ -134,6 +134,13 @@ int fi_plan_bounds(int32_t batch_size, int64_t total_qo, int32_t num_qo_heads,
  *   out_dtype  storage type of o (FI_F32 or FI_BF16; bf16 rounds to nearest even)
  *   sm_scale   logit scale; <= 0 selects 1/sqrt(head_dim)
  *   logits_soft_cap  cap of s = cap * tanh(s / cap); 0 disables it
+ *   graph_safe nonzero: every kernel of the call is launched whether or not
+ *              this plan gives it work (kernels without work exit at once),
+ *              so a call captured into a HIP graph stays valid when replayed
+ *              with any later plan of the same shapes and worker counts
+ *              (serving-engine page, "How FlashInfer Works": load balancing
+ *              that survives CUDA graphs).  0: kernels without work are not
+ *              launched.
  */
 typedef struct fi_attn_params {
   fi_dtype dtype;
@@ -144,6 +151,7 @@ typedef struct fi_attn_params {
   int32_t page_size;
   float sm_scale;
   float logits_soft_cap;
+  int32_t graph_safe;
 } fi_attn_params;
 
 /*

@@ -83,7 +83,8 @@ class fi_attn_params(ctypes.Structure):
                 ("head_dim", ctypes.c_int32),
                 ("page_size", ctypes.c_int32),
                 ("sm_scale", ctypes.c_float),
-                ("logits_soft_cap", ctypes.c_float)]
+                ("logits_soft_cap", ctypes.c_float),
+                ("graph_safe", ctypes.c_int32)]
 
 
 _lib = None
@@ -227,10 +228,12 @@ def fi_plan_bounds(batch_size, total_qo, num_qo_heads, num_kv_heads, head_dim, w
 
 
 def make_params(q_dtype, out_dtype, num_qo_heads, num_kv_heads, head_dim, page_size, sm_scale=0.0,
-                logits_soft_cap=0.0) -> fi_attn_params:
+                logits_soft_cap=0.0, graph_safe=False) -> fi_attn_params:
+    """``graph_safe``: launch every kernel of a call whatever the plan, so a
+    call captured into a graph stays valid for later plans of the same shapes."""
     return fi_attn_params(_dtype_code(q_dtype), _dtype_code(out_dtype), num_qo_heads,
                           num_kv_heads, head_dim, page_size, float(sm_scale),
-                          float(logits_soft_cap))
+                          float(logits_soft_cap), int(bool(graph_safe)))
 
 
 def fi_batch_decode_paged(plan: Plan, plan_dev, params: fi_attn_params, q, kv_pool,

@@ -99,14 +99,17 @@ RunArgs base_args(const int32_t* plan_dev, const fi_attn_params* p, const void* 
   return a;
 }
 
-// Decode stream, prefill stream, then the merges of split rows.  A kernel is
-// launched only when its stream holds rows (merges: split rows), as read from
-// the host copy of the plan; every launch keeps the fixed grid of its stream.
-int run_plan(RunArgs a, const int32_t* ph, bool with_prefill) {
+// Decode stream, prefill stream, then the merges of split rows, each with the
+// fixed grid of its stream.  A kernel is launched when its stream holds rows
+// (merges: split rows), as read from the host copy of the plan; with
+// graph_safe, whenever the call kind and dtype can use it, so that a captured
+// call launches the same kernels for every later plan.
+int run_plan(RunArgs a, const int32_t* ph, bool with_prefill, bool graph_safe) {
   int rc;
-  const bool dec = ph[H_STREAM0 + S_NROWS] != 0;
-  const bool pre = with_prefill && ph[H_STREAM1 + S_NROWS] != 0;
-  if (pre && a.dtype != FI_BF16) return set_error(FI_ERR_UNSUPPORTED, "prefill tiles need bf16 q / kv");
+  if (with_prefill && ph[H_STREAM1 + S_NROWS] != 0 && a.dtype != FI_BF16)
+    return set_error(FI_ERR_UNSUPPORTED, "prefill tiles need bf16 q / kv");
+  const bool dec = graph_safe || ph[H_STREAM0 + S_NROWS] != 0;
+  const bool pre = with_prefill && (graph_safe ? a.dtype == FI_BF16 : ph[H_STREAM1 + S_NROWS] != 0);
   a.stream_at = H_STREAM0;
   a.workers = ph[H_STREAM0 + S_W];
   a.max_tasks = a.workers - 1;
@@ -116,8 +119,8 @@ int run_plan(RunArgs a, const int32_t* ph, bool with_prefill) {
   b.max_tasks = b.workers - 1;
   if (dec && (rc = launch_decode(a))) return rc;
   if (pre && (rc = launch_prefill(b))) return rc;
-  if (dec && ph[H_STREAM0 + S_NSPLIT] != 0 && (rc = launch_merge_partials(a))) return rc;
-  if (pre && ph[H_STREAM1 + S_NSPLIT] != 0 && (rc = launch_merge_partials(b))) return rc;
+  if (dec && (graph_safe || ph[H_STREAM0 + S_NSPLIT] != 0) && (rc = launch_merge_partials(a))) return rc;
+  if (pre && (graph_safe || ph[H_STREAM1 + S_NSPLIT] != 0) && (rc = launch_merge_partials(b))) return rc;
   return FI_OK;
 }
 
@@ -180,7 +183,7 @@ int fi_batch_decode_paged(const int32_t* plan_host, const int32_t* plan_dev,
                      "fi_batch_decode_paged: plan has multi-query requests; use fi_batch_prefill_paged");
   RunArgs a = base_args(plan_dev, params, q, kv_pool, pool_pages, nullptr, kv_indptr, kv_indices,
                         kv_last_page_len, o, lse, float_ws, params->out_dtype, plan_host, stream);
-  return run_plan(a, plan_host, false);
+  return run_plan(a, plan_host, false, params->graph_safe != 0);
 }
 
 int fi_batch_prefill_paged(const int32_t* plan_host, const int32_t* plan_dev,
@@ -197,7 +200,7 @@ int fi_batch_prefill_paged(const int32_t* plan_host, const int32_t* plan_dev,
     return set_error(FI_ERR_INVALID_ARG, "fi_batch_prefill_paged: null qo_indptr");
   RunArgs a = base_args(plan_dev, params, q, kv_pool, pool_pages, qo_indptr, kv_indptr, kv_indices,
                         kv_last_page_len, o, lse, float_ws, params->out_dtype, plan_host, stream);
-  return run_plan(a, plan_host, true);
+  return run_plan(a, plan_host, true, params->graph_safe != 0);
 }
 
 int fi_merge_state(const void* v_a, const float* s_a, const void* v_b, const float* s_b,
@@ -268,10 +271,10 @@ int fi_cascade(const int32_t* plan0_host, const int32_t* plan0_dev, const int32_
 
   RunArgs a0 = base_args(plan0_dev, params, q, kv_pool, pool_pages, qo_indptr0, kv_indptr0,
                          kv_indices0, kv_last_page_len0, o0, l0, ws0, FI_F32, plan0_host, stream);
-  if ((rc = run_plan(a0, plan0_host, true))) return rc;
+  if ((rc = run_plan(a0, plan0_host, true, params->graph_safe != 0))) return rc;
   RunArgs a1 = base_args(plan1_dev, params, q, kv_pool, pool_pages, qo_indptr1, kv_indptr1,
                          kv_indices1, kv_last_page_len1, o1, l1, ws1, FI_F32, plan1_host, stream);
-  if ((rc = run_plan(a1, plan1_host, true))) return rc;
+  if ((rc = run_plan(a1, plan1_host, true, params->graph_safe != 0))) return rc;
   float* lse_out = lse ? lse : l1;  // without a caller lse, merge it in place
   return launch_merge_state(o0, l0, o1, l1, o, lse_out, rows, params->head_dim, FI_F32,
                             params->out_dtype, stream);
