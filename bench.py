@@ -276,6 +276,7 @@ def secondary_measurements(args):
         "ms": round(ms, 4), "gbs": round(nb / (ms * 1e-3) / 1e9, 1),
         "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
         "roofline_frac": round(max(nb / (HBM_PEAK_GBS * 1e9), fl / (BF16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3), 4)}
+    out["append"] = time_append(b, args.side_steps)
     del b, ps
     cb = wl.shared_prefix_cascade()
     ms_flat, _ = time_batch_call(cb.flat, args.side_steps, 3)
@@ -284,6 +285,52 @@ def secondary_measurements(args):
                       "cascade_us": round(ms_casc * 1e3, 2), "flat_us": round(ms_flat * 1e3, 2),
                       "speedup": round(ms_flat / ms_casc, 3)}
     return out
+
+
+def time_append(b, steps):
+    """Paged KV append of a step's new tokens (fi_append_paged_kv), timed with
+    HIP events on its stream: the mixed step's new tokens (every query
+    token's K/V row) into its pool, and one 32768-token prefill's.  Bytes =
+    each token row read once and written once, for K and V."""
+    import torch
+
+    import paged_kv_block_bsr_amd as fi
+    dev = torch.device("cuda", 0)
+    Hk, D, P = b.num_kv_heads, b.head_dim, b.page_size
+    esz = 2 if b.dtype == torch.bfloat16 else 4
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+    rng = np.random.default_rng(1006)
+    res = {}
+    long_pages = 32768 // P
+    cases = {
+        "mixed_step_new_tokens": (b.qo_lens, b.kv_indptr, b.kv_indices, b.kv_last_page_len, b.kv_pool.to(dev)),
+        "prefill_32768": (np.array([32768]), np.array([0, long_pages], np.int32),
+                          rng.permutation(long_pages + 8)[:long_pages].astype(np.int32), np.array([P], np.int32),
+                          torch.zeros((long_pages + 8, 2, P, Hk, D), dtype=b.dtype, device=dev)),
+    }
+    for name, (new, kv_ip, kv_idx, last, pool) in cases.items():
+        n = int(np.sum(new))
+        a_ip = np.zeros(len(new) + 1, np.int32)
+        a_ip[1:] = np.cumsum(new)
+        k = torch.randn((n, Hk, D), device=dev).to(b.dtype)
+        v = torch.randn((n, Hk, D), device=dev).to(b.dtype)
+        args = (k, v, i32(a_ip), pool, i32(kv_ip), i32(kv_idx), i32(last))
+        for _ in range(3):
+            fi.fi_append_paged_kv(*args)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for s, e in ev:
+            s.record()
+            fi.fi_append_paged_kv(*args)
+            e.record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+        nbytes = 2 * 2 * n * Hk * D * esz
+        res[name] = {"tokens": n, "bytes": nbytes, "us": round(ms * 1e3, 2),
+                     "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del args, pool
+    return res
 
 
 def prefill_only(args):

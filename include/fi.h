@@ -239,6 +239,39 @@ int fi_cascade(const int32_t* plan0_host, const int32_t* plan0_dev, const int32_
 int64_t fi_cascade_workspace_bytes(const int32_t* plan0_host, const int32_t* plan1_host);
 
 /* Thread-local message of the last error of this thread ("" if none). */
+/*
+ * Paged KV append: write a step's new K/V tokens into their pages
+ * (serving-engine page, "Dynamic Problem Shapes": the append stage, adding
+ * new tokens to the KV cache; "Page-Level Attention": a request's tokens
+ * fill the pages of its page table in order, page_size tokens per page).
+ * The index arrays describe each request's pages after the append: request
+ * i holds kv_len_i = (pages_i - 1) * page_size + kv_last_page_len[i] tokens
+ * (0 without pages), and its n_i = append_indptr[i+1] - append_indptr[i] new
+ * tokens are the last n_i of them.  New token t goes to position
+ * p = kv_len_i - n_i + t: page kv_indices[kv_indptr[i] + p / page_size],
+ * slot p % page_size, K at index 0 and V at index 1 of the pool's axis 1.
+ *   append_k, append_v  device [n_tokens, num_kv_heads, head_dim] (dtype)
+ *   append_indptr       device int32 [batch_size + 1], append_indptr[0] = 0,
+ *                       append_indptr[batch_size] = n_tokens, non-decreasing
+ *   kv_pool             device [pool_pages, 2, page_size, num_kv_heads,
+ *                       head_dim] (dtype), written in place
+ *   kv_indptr, kv_indices (kv_indices_len entries), kv_last_page_len:
+ *                       device int32 arrays of the page table
+ * On the device, a token whose position would be negative (more new tokens
+ * than the request holds), whose page-table entry lies outside kv_indices,
+ * or whose page id is not below pool_pages is not written.  Returns
+ * FI_ERR_INVALID_ARG for negative sizes, null pointers with tokens to write,
+ * or buffers that are not 16-byte aligned; FI_ERR_UNSUPPORTED for a dtype
+ * other than FI_F32 / FI_BF16 or a token row (num_kv_heads * head_dim
+ * elements) that is not a multiple of 16 bytes.  Nothing is launched on
+ * error, nor when n_tokens is 0.
+ */
+int fi_append_paged_kv(const void* append_k, const void* append_v, fi_dtype dtype,
+                       const int32_t* append_indptr, int32_t batch_size, int64_t n_tokens,
+                       void* kv_pool, int64_t pool_pages, int32_t page_size, int32_t num_kv_heads,
+                       int32_t head_dim, const int32_t* kv_indptr, const int32_t* kv_indices,
+                       int64_t kv_indices_len, const int32_t* kv_last_page_len, void* stream);
+
 const char* fi_last_error(void);
 
 /* Library version, major * 10000 + minor * 100 + patch. */

@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     FIError,
     Plan,
     decode_plan_buffer,
+    fi_append_paged_kv,
     fi_batch_decode_paged,
     fi_batch_prefill_paged,
     fi_cascade,

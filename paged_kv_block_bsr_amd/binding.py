@@ -38,8 +38,8 @@ H_STREAM0, H_STREAM1 = 12, 32
  S_OFF_WIP, S_OFF_MERGE, S_OFF_SPLIT, S_WS_O, S_WS_LSE, S_KIND, S_OFF_META) = range(17)
 
 EXPORTS = ["fi_plan", "fi_plan_bounds", "fi_batch_decode_paged", "fi_batch_prefill_paged",
-           "fi_merge_state", "fi_cascade", "fi_cascade_workspace_bytes", "fi_last_error",
-           "fi_version", "fi_default_workers"]
+           "fi_merge_state", "fi_cascade", "fi_cascade_workspace_bytes", "fi_append_paged_kv",
+           "fi_last_error", "fi_version", "fi_default_workers"]
 
 
 class FIError(RuntimeError):
@@ -113,6 +113,9 @@ def lib():
                                  ctypes.POINTER(fi_attn_params), vp, vp, ctypes.c_int64, vp, vp, vp,
                                  ctypes.c_int64, vp]
         L.fi_cascade_workspace_bytes.argtypes = [vp, vp]
+        L.fi_append_paged_kv.argtypes = [vp, vp, ctypes.c_int, vp, ctypes.c_int32, ctypes.c_int64, vp,
+                                         ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         vp, vp, ctypes.c_int64, vp, vp]
         L.fi_cascade_workspace_bytes.restype = ctypes.c_int64
         L.fi_last_error.restype = ctypes.c_char_p
         L.fi_default_workers.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
@@ -278,6 +281,24 @@ def fi_cascade(plan0: Plan, plan0_dev, qo_indptr0, kv_indptr0, kv_indices0, kv_l
         _ptr(kv_indptr1), _ptr(kv_indices1), _ptr(kv_last_page_len1), ctypes.byref(params),
         _ptr(q), _ptr(kv_pool), kv_pool.shape[0], _ptr(o), _ptr(lse), _ptr(float_ws),
         float_ws.numel() * float_ws.element_size(), _stream(stream)))
+
+
+def fi_append_paged_kv(append_k, append_v, append_indptr, kv_pool, kv_indptr, kv_indices,
+                       kv_last_page_len, stream=None):
+    """Write new K/V rows ``[n_tokens, Hk, D]`` into their pages of ``kv_pool``
+    ``[pages, 2, P, Hk, D]`` (``fi_append_paged_kv``); index arrays are device int32."""
+    n, hk, d = append_k.shape
+    pages, two, page_size, hk2, d2 = kv_pool.shape
+    if (append_v.shape != append_k.shape or two != 2 or (hk2, d2) != (hk, d)
+            or append_v.dtype != append_k.dtype or kv_pool.dtype != append_k.dtype):
+        raise FIError(FI_ERR_INVALID_ARG, "fi_append_paged_kv: shapes or dtypes disagree")
+    for t in (append_k, append_v, kv_pool, append_indptr, kv_indptr, kv_indices, kv_last_page_len):
+        if not t.is_contiguous():
+            raise FIError(FI_ERR_INVALID_ARG, "fi_append_paged_kv: tensors must be contiguous")
+    _check(lib().fi_append_paged_kv(_ptr(append_k), _ptr(append_v), _dtype_code(append_k.dtype),
+                                    _ptr(append_indptr), append_indptr.numel() - 1, n, _ptr(kv_pool),
+                                    pages, page_size, hk, d, _ptr(kv_indptr), _ptr(kv_indices),
+                                    kv_indices.numel(), _ptr(kv_last_page_len), _stream(stream)))
 
 
 def fi_last_error() -> str:

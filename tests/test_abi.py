@@ -179,3 +179,15 @@ def test_run_calls_reject_bad_arguments_without_a_gpu():
     rc = L.fi_batch_decode_paged(bad.ctypes.data, 16, ctypes.byref(params), 16, 16, 10, 16, 16, 16,
                                  16, None, 16, 1 << 20, None)
     assert rc == fi.binding.FI_ERR_PLAN_MISMATCH
+
+
+def test_append_rejects_bad_arguments():
+    L = fi.lib()
+    args = lambda dtype=fi.FI_BF16, n=5, hk=8, d=128: (None, None, dtype, None, 1, n, None, 1, 16, hk, d,
+                                                        None, None, 1, None, None)
+    assert L.fi_append_paged_kv(*args(dtype=7)) == -2            # dtype
+    assert L.fi_append_paged_kv(*args(n=-1)) == -1               # negative size
+    assert L.fi_append_paged_kv(*args(n=0)) == 0                 # nothing to write: no launch
+    assert L.fi_append_paged_kv(*args()) == -1                   # null pointers with tokens
+    assert L.fi_append_paged_kv(*args(hk=1, d=4)) == -2          # 8-byte rows
+    assert "token row" in fi.fi_last_error()
