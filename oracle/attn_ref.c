@@ -32,7 +32,12 @@
  *     qo_len queries and kv_len keys sees keys j <= kv_len - qo_len + t;
  *   - the soft-cap applies to the already-scaled logit;
  *   - a row with no visible key has o = 0 and lse = -inf;
- *   - lse is the natural-log log-sum-exp of the (capped) logits.
+ *   - lse is the natural-log log-sum-exp of the (capped) logits;
+ *   - sliding window (paper page, opening paragraph: sliding windows among the
+ *     attention variants; "Customizable attention": a variant is a mask):
+ *     with window_left >= 0 the query at position kv_len - qo_len + t sees no
+ *     key more than window_left positions before it (window_left < 0: no
+ *     window).
  *
  * Parity pins: see the oracle tests (dense brute force, library SDPA, closed
  * forms, the pages' page-table example, page-permutation invariance,
@@ -139,7 +144,7 @@ static inline double pool_at(const double *pool, int64_t page, int kv, int64_t s
 int oref_attention_rows(int B, const int32_t *qo_indptr, const int32_t *kv_indptr,
                         const int32_t *kv_indices, const int32_t *kv_last_page_len, int P,
                         int Hq, int Hk, int D, int causal, double sm_scale, double soft_cap,
-                        const double *q, const double *pool, int64_t pool_pages,
+                        int window_left, const double *q, const double *pool, int64_t pool_pages,
                         int64_t n_rows, const int32_t *row_req, const int32_t *row_tok,
                         const int32_t *row_head, double *o, double *lse) {
   int rc = oref_validate(B, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, P, Hq, Hk, D,
@@ -162,14 +167,18 @@ int oref_attention_rows(int B, const int32_t *qo_indptr, const int32_t *kv_indpt
     const int64_t kv_len = kv_len_of(kv_indptr, kv_last_page_len, i, P);
     const int64_t qo_len = qo_len_of(qo_indptr, i);
     const int64_t limit = causal ? kv_len - qo_len + t + 1 : kv_len;
+    /* sliding window: the query sits at position kv_len - qo_len + t and
+       sees no key more than window_left positions before it */
+    int64_t first = 0;
+    if (window_left >= 0 && kv_len - qo_len + t - window_left > 0) first = kv_len - qo_len + t - window_left;
     const double *qrow = q + ((qo_start_of(qo_indptr, i) + t) * (int64_t)Hq + h) * D;
     double *orow = o + r * (int64_t)D;
-    if (limit <= 0) {
+    if (limit <= first) {
       for (int d = 0; d < D; ++d) orow[d] = 0.0;
       lse[r] = -INFINITY;
       continue;
     }
-    double *s = (double *)malloc(sizeof(double) * (size_t)limit);
+    double *s = (double *)malloc(sizeof(double) * (size_t)(limit - first));
     if (!s) {
 #pragma omp critical
       rc_all = OREF_ENOMEM;
@@ -177,23 +186,23 @@ int oref_attention_rows(int B, const int32_t *qo_indptr, const int32_t *kv_indpt
     }
     /* pass 1: logits of every visible key, gathered one token at a time */
     double m = -INFINITY;
-    for (int64_t j = 0; j < limit; ++j) {
+    for (int64_t j = first; j < limit; ++j) {
       int64_t page = kv_indices[kv_indptr[i] + j / P];
       int64_t slot = j % P;
       double acc = 0.0;
       for (int d = 0; d < D; ++d) acc += qrow[d] * pool_at(pool, page, 0, slot, g, d, P, Hk, D);
       acc *= sm_scale;
       if (soft_cap > 0.0) acc = soft_cap * tanh(acc / soft_cap);
-      s[j] = acc;
+      s[j - first] = acc;
       if (acc > m) m = acc;
     }
     /* pass 2: normaliser and weighted sum of values */
     double z = 0.0;
     for (int d = 0; d < D; ++d) orow[d] = 0.0;
-    for (int64_t j = 0; j < limit; ++j) {
+    for (int64_t j = first; j < limit; ++j) {
       int64_t page = kv_indices[kv_indptr[i] + j / P];
       int64_t slot = j % P;
-      double w = exp(s[j] - m);
+      double w = exp(s[j - first] - m);
       z += w;
       for (int d = 0; d < D; ++d) orow[d] += w * pool_at(pool, page, 1, slot, g, d, P, Hk, D);
     }
@@ -209,8 +218,8 @@ int oref_attention_rows(int B, const int32_t *qo_indptr, const int32_t *kv_indpt
  */
 int oref_attention(int B, const int32_t *qo_indptr, const int32_t *kv_indptr,
                    const int32_t *kv_indices, const int32_t *kv_last_page_len, int P, int Hq,
-                   int Hk, int D, int causal, double sm_scale, double soft_cap, const double *q,
-                   const double *pool, int64_t pool_pages, double *o, double *lse) {
+                   int Hk, int D, int causal, double sm_scale, double soft_cap, int window_left,
+                   const double *q, const double *pool, int64_t pool_pages, double *o, double *lse) {
   int64_t total = 0;
   for (int i = 0; i < B; ++i) total += qo_len_of(qo_indptr, i);
   int64_t n = total * Hq;
@@ -228,8 +237,8 @@ int oref_attention(int B, const int32_t *qo_indptr, const int32_t *kv_indptr,
         rq[r] = i; rt[r] = (int32_t)t; rh[r] = h; ++r;
       }
   int rc = oref_attention_rows(B, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, P, Hq, Hk,
-                               D, causal, sm_scale, soft_cap, q, pool, pool_pages, n, rq, rt, rh,
-                               o, lse);
+                               D, causal, sm_scale, soft_cap, window_left, q, pool, pool_pages, n,
+                               rq, rt, rh, o, lse);
   free(rq); free(rt); free(rh);
   return rc;
 }

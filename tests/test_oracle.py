@@ -391,3 +391,84 @@ def test_oracle_rejects_invalid_index_arrays(mutate):
         pb["kv_indices"][0] = pb["pool"].shape[0]
     with pytest.raises(ref.OracleError):
         run_oracle(pb, P, Hq, Hk, D, causal, 1.0, 0.0)
+
+
+# --------------------------------------------------------------------------
+# Sliding window (paper page: sliding windows among the attention variants,
+# a variant being a mask).  Pins: a window as long as the request changes
+# nothing; window 0 leaves the query's own key (closed form); and every query
+# row equals the unwindowed oracle on a truncated copy of its visible keys.
+# --------------------------------------------------------------------------
+
+def _window_batch(seed, qo, kv, P, causal, cap=0.0):
+    import workloads as wl
+    return wl.make_batch(seed, qo, kv, page_size=P, num_qo_heads=4, num_kv_heads=2, head_dim=8,
+                         dtype=torch.float32, causal=causal, soft_cap=cap)
+
+
+def _keys_of(b, i):
+    """Request i's K and V rows [kv_len, Hk, D], gathered token by token."""
+    pool = b.kv_pool.numpy()
+    n = int(b.kv_indptr[i + 1] - b.kv_indptr[i])
+    L = 0 if n == 0 else (n - 1) * b.page_size + int(b.kv_last_page_len[i])
+    pages = b.kv_indices[b.kv_indptr[i]:b.kv_indptr[i + 1]]
+    j = np.arange(L)
+    return pool[pages[j // b.page_size], 0, j % b.page_size], pool[pages[j // b.page_size], 1, j % b.page_size]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_window_as_long_as_the_request_changes_nothing(causal):
+    b = _window_batch(501, [1, 3, 7], [40, 19, 7], 4, causal)
+    o0, l0 = ref.attention_of(b)
+    o1, l1 = ref.attention_of(b, window_left=40)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_window_zero_keeps_the_querys_own_key():
+    b = _window_batch(502, [1, 5], [23, 9], 4, True, cap=7.0)
+    o, lse = ref.attention_of(b, window_left=0)
+    qo = b.qo_indptr
+    for i in range(2):
+        K, V = _keys_of(b, i)
+        L, n = K.shape[0], qo[i + 1] - qo[i]
+        for t in range(n):
+            p = L - n + t
+            for h in range(4):
+                g = h // 2
+                s = b.sm_scale * float(np.dot(b.q[qo[i] + t, h].double().numpy(), K[p, g]))
+                s = 7.0 * math.tanh(s / 7.0)
+                assert np.allclose(o[qo[i] + t, h], V[p, g], rtol=0, atol=1e-12)
+                assert abs(lse[qo[i] + t, h] - s) < 1e-12
+
+
+@pytest.mark.parametrize("causal,cap", [(True, 0.0), (False, 0.0), (True, 9.0)])
+def test_window_equals_attention_over_the_visible_keys_alone(causal, cap):
+    import workloads as wl
+    b = _window_batch(503, [1, 6, 4, 2], [37, 30, 4, 18], 4, causal, cap)
+    for w in (1, 3, 8, 17):
+        o, lse = ref.attention_of(b, window_left=w)
+        qo = b.qo_indptr
+        for i in range(4):
+            K, V = _keys_of(b, i)
+            L, n = K.shape[0], qo[i + 1] - qo[i]
+            for t in range(n):
+                p = L - n + t
+                hi = p + 1 if causal else L
+                keep = np.arange(max(0, p - w), hi)
+                # one query over exactly the kept keys, one token per page, no mask
+                m = len(keep)
+                pool = np.zeros((m, 2, 1, 2, 8), np.float32)
+                pool[:, 0, 0] = K[keep]
+                pool[:, 1, 0] = V[keep]
+                sub = wl.PagedBatch(page_size=1, num_qo_heads=4, num_kv_heads=2, head_dim=8,
+                                    dtype=torch.float32, causal=False, sm_scale=b.sm_scale,
+                                    soft_cap=cap, qo_lens=np.array([1]), kv_lens=np.array([m]),
+                                    qo_indptr=np.array([0, 1], np.int32),
+                                    kv_indptr=np.array([0, m], np.int32),
+                                    kv_indices=np.arange(m, dtype=np.int32),
+                                    kv_last_page_len=np.array([1], np.int32),
+                                    q=b.q[qo[i] + t:qo[i] + t + 1].clone(),
+                                    kv_pool=torch.from_numpy(pool))
+                o_s, l_s = ref.attention_of(sub)
+                assert np.allclose(o[qo[i] + t], o_s[0], rtol=0, atol=1e-12), (w, i, t)
+                assert np.allclose(lse[qo[i] + t], l_s[0], rtol=0, atol=1e-12), (w, i, t)
