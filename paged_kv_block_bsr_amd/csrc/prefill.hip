@@ -63,13 +63,15 @@ __device__ __forceinline__ uint32_t pack_f16_rtz(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
 }
 
-// max of three floats as one v_max3_f32.  Written out so that the compiler
-// does not quieten each input first: the logits it is applied to are finite
-// or -inf (masked), never NaN.
+// max of three floats as one v_maximum3_f32 (NaN-propagating maximum, which
+// needs no quietening of its inputs as fmaxf does; the logits it is applied
+// to are finite or -inf, never NaN).  It stays a compiler builtin, not inline
+// asm: its inputs come straight from matrix-core results, and only for code
+// it can see does the compiler insert the wait states that must separate an
+// MFMA from a VALU read of its result.  (An asm form read the accumulators
+// too early, a timing-dependent stale max.)
 __device__ __forceinline__ float max3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
 // v_permlane32_swap on (x, x) leaves x of lane l % 32 in one result and x of

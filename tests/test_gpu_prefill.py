@@ -122,3 +122,25 @@ def test_fp32_batch_of_single_queries_through_prefill_call():
     note("fp32 single-query rows through fi_batch_prefill_paged")
     o, lse, _ = run(b, workers_decode=2, workers_prefill=2, min_seg_pages=1)
     assert_close(o, lse, o_ref, l_ref, "fp32 prefill call")
+
+
+def test_prefill_repeats_bit_exactly_with_two_workgroups_per_cu():
+    """64 tiles on 64 workers x 8 KV heads: 512 busy workgroups, two per CU.
+    Repeated calls give identical bits (the kernel reads no matrix-core
+    result before the wait states that must follow an MFMA, whatever the
+    other wave on the SIMD does)."""
+    b = wl.make_batch(71, [256] * 8, [1024 + 256] * 8, page_size=16, num_qo_heads=32,
+                      num_kv_heads=8, head_dim=128, dtype=torch.bfloat16, causal=True)
+    dev = DeviceBatch(b)
+    outs = []
+    for k in range(4):
+        note(f"repeat {k}: 512 busy prefill workgroups")
+        o, lse, plan = run(b, workers_decode=1, workers_prefill=64, no_split=1, dev=dev)
+        outs.append((o, lse))
+    assert plan.info.prefill_items == 64
+    for o, lse in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
+    rows = _rows_for(b)
+    o_ref, l_ref = ref.attention_rows_of(b, rows)
+    og, lg = _gather(outs[0][0], outs[0][1], b, rows)
+    assert_close(og, lg, o_ref, l_ref, "512 busy workgroups")
