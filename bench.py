@@ -60,13 +60,23 @@ def counter_traffic(workload):
     return int(d["traffic_bytes_per_dispatch"])
 
 
-def decode_bytes(b) -> int:
-    """Algorithmic bytes of one decode pass (the method's own traffic)."""
+def decode_bytes(b, window_left=-1) -> int:
+    """Algorithmic bytes of one decode pass (the method's own traffic).  With a
+    sliding window only the keys inside it, and the page-table entries of
+    their pages, are counted."""
     esz = 2 if b.dtype.itemsize == 2 else 4
-    kv = int(b.kv_lens.sum()) * b.num_kv_heads * 2 * b.head_dim * esz
+    kv_lens = b.kv_lens.astype(np.int64)
+    if window_left >= 0:
+        first = np.maximum(kv_lens - 1 - window_left, 0)
+        keys = int((kv_lens - first).sum())
+        P = b.page_size
+        pages = int((-(-kv_lens // P) - first // P).sum())
+    else:
+        keys, pages = int(kv_lens.sum()), len(b.kv_indices)
+    kv = keys * b.num_kv_heads * 2 * b.head_dim * esz
     qo = 2 * b.total_qo * b.num_qo_heads * b.head_dim * esz
     lse = b.total_qo * b.num_qo_heads * 4
-    idx = 4 * (len(b.kv_indices) + len(b.kv_indptr) + len(b.kv_last_page_len))
+    idx = 4 * (pages + len(b.kv_indptr) + len(b.kv_last_page_len))
     return kv + qo + lse + idx
 
 
@@ -169,14 +179,16 @@ def run_decode_bench(args):
     return result, b, nbytes
 
 
-def prefill_flops(b) -> int:
-    """Causal-visible flops: 4 D per (query head, visible key) pair (QK^T and PV)."""
+def prefill_flops(b, window_left=-1) -> int:
+    """Visible flops: 4 D per (query head, visible key) pair (QK^T and PV).
+    Query t of a request sees keys up to p = kv - qo + t (causal) or kv - 1,
+    and with a sliding window none before p - window_left."""
     tot = 0
     for qo, kv in zip(b.qo_lens.tolist(), b.kv_lens.tolist()):
-        if b.causal:
-            tot += qo * (kv - qo) + qo * (qo + 1) // 2
-        else:
-            tot += qo * kv
+        p = kv - qo + np.arange(qo, dtype=np.int64)
+        hi = p + 1 if b.causal else np.full(qo, kv, np.int64)
+        lo = np.maximum(p - window_left, 0) if window_left >= 0 else np.zeros(qo, np.int64)
+        tot += int(np.maximum(hi - lo, 0).sum())
     return 4 * b.head_dim * b.num_qo_heads * tot
 
 
@@ -205,7 +217,8 @@ def prefill_slice(b):
                          q=torch.cat(qrows), kv_pool=b.kv_pool, name=b.name + "/prefill_slice")
 
 
-def time_batch_call(b, steps, warmup, workers_decode=0, workers_prefill=0, pool_copies=2):
+def time_batch_call(b, steps, warmup, workers_decode=0, workers_prefill=0, pool_copies=2,
+                    window_left=-1):
     """Plan once, then time the run call (decode/prefill kernels + merges) with
     HIP events on its stream.  Returns (mean ms, plan)."""
     import torch
@@ -217,7 +230,8 @@ def time_batch_call(b, steps, warmup, workers_decode=0, workers_prefill=0, pool_
     wp = workers_prefill or fi.fi_default_workers(fi.FI_KIND_PREFILL, NUM_CUS, Hk)
     plan = fi.fi_plan(b.qo_indptr, b.kv_indptr, b.kv_last_page_len, page_size=b.page_size,
                       num_qo_heads=b.num_qo_heads, num_kv_heads=Hk, head_dim=b.head_dim,
-                      causal=b.causal, workers_decode=wd, workers_prefill=wp)
+                      causal=b.causal, workers_decode=wd, workers_prefill=wp,
+                      window_left=window_left)
     plan_dev = plan.to_device(dev)
     i32 = lambda a: torch.from_numpy(np.asarray(a, np.int32)).to(dev)
     pools = [b.kv_pool.to(dev) for _ in range(max(1, pool_copies))]
@@ -277,6 +291,7 @@ def secondary_measurements(args):
         "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
         "roofline_frac": round(max(nb / (HBM_PEAK_GBS * 1e9), fl / (BF16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3), 4)}
     out["append"] = time_append(b, args.side_steps)
+    out["window"] = window_measurements(ps, args.side_steps)
     del b, ps
     cb = wl.shared_prefix_cascade()
     ms_flat, _ = time_batch_call(cb.flat, args.side_steps, 3)
@@ -284,6 +299,31 @@ def secondary_measurements(args):
     out["cascade"] = {"workload": "shared_prefix_cascade (64 requests, 2048-token prefix, soft-cap 30)",
                       "cascade_us": round(ms_casc * 1e3, 2), "flat_us": round(ms_flat * 1e3, 2),
                       "speedup": round(ms_flat / ms_casc, 3)}
+    return out
+
+
+WINDOW = 1023  # keys a query sees before its own (a 1024-key sliding window)
+
+
+def window_measurements(ps, steps):
+    """Sliding-window attention with a 1024-key window: the decode workload
+    (each request reads its last <= 1024 keys) and the prefill slice of the
+    mixed step.  Only keys inside the window count as work."""
+    import workloads as wl
+    db = wl.llama8b_decode()
+    ms, plan = time_batch_call(db, steps, 3, window_left=WINDOW)
+    nb = decode_bytes(db, WINDOW)
+    out = {"window_left": WINDOW,
+           "decode": {"workload": "llama8b_decode, window 1023", "us": round(ms * 1e3, 2),
+                      "bytes": nb, "gbs": round(nb / (ms * 1e-3) / 1e9, 1),
+                      "frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+    del db
+    ms, plan = time_batch_call(ps, steps, 3, window_left=WINDOW)
+    fl = prefill_flops(ps, WINDOW)
+    out["prefill_slice"] = {"workload": "mixed_ragged_step prefill requests, window 1023",
+                            "ms": round(ms, 4), "flops": fl,
+                            "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                            "frac": round(fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
     return out
 
 

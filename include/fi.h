@@ -81,6 +81,16 @@ typedef enum fi_dtype { FI_F32 = 0, FI_BF16 = 1 } fi_dtype;
  *   min_seg_pages     >= 1, smallest segment of the page stream one worker owns
  *   br_override       0 (tile rows from the mean query length) or 16/32/64/128
  *   no_split          1: one item per row, no partial slots (unsplit reference)
+ *   window_left       -1: no window.  >= 0: sliding-window attention, the
+ *                     query at position p = kv_len - qo_len + t sees no key
+ *                     before p - window_left (paper page: sliding windows
+ *                     among the attention variants of its opening paragraph;
+ *                     "Customizable attention": a variant is a logits mask).
+ *                     The plan drops every page no query of a row can see and
+ *                     records the window; the run calls apply it.  Every
+ *                     request needs kv_len + qo_len < 2^30 (else
+ *                     FI_ERR_UNSUPPORTED).  The cascade call takes no
+ *                     windowed plan.
  */
 typedef struct fi_plan_in {
   int32_t batch_size;
@@ -97,6 +107,7 @@ typedef struct fi_plan_in {
   int32_t min_seg_pages;
   int32_t br_override;
   int32_t no_split;
+  int32_t window_left;
 } fi_plan_in;
 
 /* Summary of a plan (also recorded inside the plan buffer). */

@@ -16,10 +16,14 @@ spells out every step:
 
 P1 validate; P2 per-request pages, kv_len, qo_len; P3 classify requests
 (qo_len 0: nothing, 1: a decode row, >= 2: prefill tiles); P4 prefill tile
-size BR; P5 rows in request order; P6 per stream, cost C = sum of visible
+size BR; P5 rows in request order, each with its first visible page fp
+(0, or with a sliding window of w keys the page of the first key the row's
+earliest query sees, max(0, kv_len - qo_len + tok_lo - w)) and its visible
+pages counted from fp; P6 per stream, cost C = sum of visible
 pages, segment size S = max(min_seg_pages, ceil(C / W)), row r occupies stream
 positions [c_r, c_r + vis_r), worker w owns [w S, (w + 1) S); P7 one item per
-(row, worker) overlap, a row without visible pages gets one empty item; P8
+(row, worker) overlap, a row without visible pages gets one empty item, and an
+item's pages are the overlap shifted by fp - c_r (pages of its request); P8
 rows with k >= 2 items get k consecutive partial slots; P9 emit int32 arrays.
 
 Parity against the pages: unpinned (they print no plan); the tests pin this
@@ -32,13 +36,15 @@ FI_ERR_INVALID_ARG = -1
 FI_ERR_UNSUPPORTED = -2
 
 MAGIC = 0x31504946
-VERSION = 1
+VERSION = 2
 HEADER_INTS = 64
 STREAM_DESC_INTS = 20
 STREAM0_AT = 12
 STREAM1_AT = 32
+WINDOW_AT = 52
 MAX_TILE_ROWS = 128
 INT32_MAX = 2 ** 31 - 1
+WINDOW_MAX_TOKENS = 2 ** 30  # a windowed request needs kv_len + qo_len below this
 
 
 def _ceil_div(a: int, b: int) -> int:
@@ -58,7 +64,7 @@ def _align64(n: int) -> int:
 
 
 def validate(B, qo_indptr, kv_indptr, kv_last_page_len, P, Hq, Hk, D, causal, W_d, W_p,
-             min_seg_pages, br_override, no_split):
+             min_seg_pages, br_override, no_split, window_left=-1):
     """P1.  Returns (code, message)."""
     if B < 0:
         return FI_ERR_INVALID_ARG, "negative batch size"
@@ -78,6 +84,8 @@ def validate(B, qo_indptr, kv_indptr, kv_last_page_len, P, Hq, Hk, D, causal, W_
         return FI_ERR_INVALID_ARG, "br_override"
     if no_split not in (0, 1):
         return FI_ERR_INVALID_ARG, "no_split"
+    if not -1 <= window_left <= INT32_MAX:
+        return FI_ERR_INVALID_ARG, "window_left"
     if len(kv_indptr) != B + 1 or len(kv_last_page_len) < B:
         return FI_ERR_INVALID_ARG, "array lengths"
     if qo_indptr is not None and len(qo_indptr) != B + 1:
@@ -100,6 +108,8 @@ def validate(B, qo_indptr, kv_indptr, kv_last_page_len, P, Hq, Hk, D, causal, W_
             return FI_ERR_INVALID_ARG, "kv_len too large"
         if causal and qo >= 2 and qo > kv:
             return FI_ERR_INVALID_ARG, "causal with qo_len > kv_len"
+        if window_left >= 0 and kv + qo >= WINDOW_MAX_TOKENS:
+            return FI_ERR_UNSUPPORTED, "window with kv_len + qo_len >= 2^30"
     return FI_OK, ""
 
 
@@ -151,7 +161,7 @@ def _partition(rows_vis, W, S, no_split):
 
 def plan(qo_indptr, kv_indptr, kv_last_page_len, *, page_size, num_qo_heads, num_kv_heads,
          head_dim, causal, workers_decode, workers_prefill, min_seg_pages=8, br_override=0,
-         no_split=0):
+         no_split=0, window_left=-1):
     """Build the plan.  Returns (code, result) where result is a dict with the
     header scalars, each stream's arrays and the flat int32 buffer."""
     B = len(kv_indptr) - 1
@@ -160,7 +170,8 @@ def plan(qo_indptr, kv_indptr, kv_last_page_len, *, page_size, num_qo_heads, num
     kv_indptr = [int(x) for x in kv_indptr]
     last = [int(x) for x in kv_last_page_len]
     code, msg = validate(B, qo_indptr, kv_indptr, last, P, Hq, Hk, D, int(bool(causal)),
-                         workers_decode, workers_prefill, min_seg_pages, br_override, no_split)
+                         workers_decode, workers_prefill, min_seg_pages, br_override, no_split,
+                         window_left)
     if code != FI_OK:
         return code, msg
     G = Hq // Hk
@@ -179,16 +190,29 @@ def plan(qo_indptr, kv_indptr, kv_last_page_len, *, page_size, num_qo_heads, num
         BR = min(MAX_TILE_ROWS, max(16, _next_pow2(mean)))
     else:
         BR = 0
-    # P5
-    rows_d = [(i, 0, G, npages[i]) for i in decode_reqs]
-    rows_p = []
+    # P5.  A row of query tokens [tok_lo, tok_hi] sees keys [first, end):
+    # end from the causal bound of tok_hi (or kv_len), first from the window
+    # bound of tok_lo (or 0).  Its pages are fp = first // P .. ceil(end / P).
+    def first_page(i, tok_lo):
+        if window_left < 0:
+            return 0
+        return max(0, kv_len[i] - qo_len[i] + tok_lo - window_left) // P
+
+    rows_d, fp_d = [], []
+    for i in decode_reqs:
+        fp = first_page(i, 0)
+        rows_d.append((i, 0, G, max(0, npages[i] - fp)))
+        fp_d.append(fp)
+    rows_p, fp_p = [], []
     for i in prefill_reqs:
         n_packed = qo_len[i] * G
         for k in range(_ceil_div(n_packed, BR)):
             rb, re = k * BR, min((k + 1) * BR, n_packed)
-            tok_hi = (re - 1) // G
-            vis = kv_len[i] - qo_len[i] + tok_hi + 1 if causal else kv_len[i]
-            rows_p.append((i, rb, re, _ceil_div(vis, P)))
+            tok_lo, tok_hi = rb // G, (re - 1) // G
+            end = kv_len[i] - qo_len[i] + tok_hi + 1 if causal else kv_len[i]
+            fp = first_page(i, tok_lo)
+            rows_p.append((i, rb, re, max(0, _ceil_div(end, P) - fp)))
+            fp_p.append(fp)
     # float workspace regions (float units, each a multiple of 64 floats)
     cap_d = 2 * (workers_decode - 1)
     cap_p = 2 * (workers_prefill - 1)
@@ -200,12 +224,15 @@ def plan(qo_indptr, kv_indptr, kv_last_page_len, *, page_size, num_qo_heads, num
         return FI_ERR_INVALID_ARG, "workspace too large for the workers given"
 
     streams = []
-    for kind, rows, W, tile in ((0, rows_d, workers_decode, G), (1, rows_p, workers_prefill, BR)):
+    for kind, rows, fps, W, tile in ((0, rows_d, fp_d, workers_decode, G),
+                                     (1, rows_p, fp_p, workers_prefill, BR)):
         vis = [r[3] for r in rows]
         C = sum(vis)
         S = max(min_seg_pages, _ceil_div(C, W))
         items, wip, merge_indptr, split_rows = _partition(vis, W, S, no_split)
-        streams.append(dict(kind=kind, W=W, S=S, BR=tile, rows=rows, items=items, wip=wip,
+        # item pages are request pages: shift by the row's first visible page
+        items = [(r, fps[r] + pb, fps[r] + pe, slot) for (r, pb, pe, slot) in items]
+        streams.append(dict(kind=kind, W=W, S=S, BR=tile, rows=rows, first_page=fps, items=items, wip=wip,
                             merge_indptr=merge_indptr, split_rows=split_rows,
                             n_slots=merge_indptr[-1],
                             slot_cap=cap_d if kind == 0 else cap_p,
@@ -239,12 +266,14 @@ def plan(qo_indptr, kv_indptr, kv_last_page_len, *, page_size, num_qo_heads, num
     head = [MAGIC, VERSION, len(buf), B, sum(qo_len), Hq, Hk, D, P, int(bool(causal)), G,
             ws_total]
     buf[:len(head)] = head
+    buf[WINDOW_AT] = window_left
     for at, st in ((STREAM0_AT, streams[0]), (STREAM1_AT, streams[1])):
         desc = [st["W"], st["S"], st["BR"], len(st["rows"]), len(st["items"]), st["n_slots"],
                 len(st["split_rows"]), st["slot_cap"], st["off_rows"], st["off_items"],
                 st["off_wip"], st["off_merge_indptr"], st["off_split"], st["ws_off_o"],
                 st["ws_off_lse"], st["kind"], st["off_item_meta"], 0, 0, 0]
         buf[at:at + STREAM_DESC_INTS] = desc
-    result = dict(B=B, total_qo=sum(qo_len), G=G, ws_floats=ws_total, decode=streams[0],
+    result = dict(B=B, total_qo=sum(qo_len), G=G, ws_floats=ws_total, window_left=window_left,
+                  decode=streams[0],
                   prefill=streams[1], buf=buf, kv_len=kv_len, qo_len=qo_len)
     return FI_OK, result

@@ -62,7 +62,8 @@ class fi_plan_in(ctypes.Structure):
                 ("workers_prefill", ctypes.c_int32),
                 ("min_seg_pages", ctypes.c_int32),
                 ("br_override", ctypes.c_int32),
-                ("no_split", ctypes.c_int32)]
+                ("no_split", ctypes.c_int32),
+                ("window_left", ctypes.c_int32)]
 
 
 class fi_plan_info(ctypes.Structure):
@@ -194,9 +195,10 @@ class Plan:
 
 def fi_plan(qo_indptr, kv_indptr, kv_last_page_len, *, page_size, num_qo_heads, num_kv_heads,
             head_dim, causal, workers_decode, workers_prefill=1, min_seg_pages=8,
-            br_override=0, no_split=0, capacity: Optional[int] = None,
+            br_override=0, no_split=0, window_left=-1, capacity: Optional[int] = None,
             out: Optional[np.ndarray] = None) -> Plan:
-    """Build a plan on the host from host index arrays (``fi_plan``)."""
+    """Build a plan on the host from host index arrays (``fi_plan``).
+    ``window_left`` >= 0: sliding-window attention (-1: none)."""
     kp = _i32_host(kv_indptr)
     kl = _i32_host(kv_last_page_len)
     qo = _i32_host(qo_indptr)
@@ -215,7 +217,8 @@ def fi_plan(qo_indptr, kv_indptr, kv_last_page_len, *, page_size, num_qo_heads, 
     buf = out if out is not None else np.zeros(capacity, np.int32)
     pin = fi_plan_in(B, qo.ctypes.data if qo is not None else None, kp.ctypes.data, kl.ctypes.data,
                      page_size, num_qo_heads, num_kv_heads, head_dim, int(bool(causal)),
-                     workers_decode, workers_prefill, min_seg_pages, br_override, no_split)
+                     workers_decode, workers_prefill, min_seg_pages, br_override, no_split,
+                     window_left)
     info = fi_plan_info()
     _check(lib().fi_plan(ctypes.byref(pin), buf.ctypes.data, len(buf), ctypes.byref(info)))
     return Plan(buf=buf, info=info)

@@ -53,6 +53,7 @@ struct DecodeParams {
   float scale;         // sm_scale
   float cap;           // soft-cap; 0 = off
   float inv_cap;       // 1 / cap (0 when off)
+  int32_t window;      // sliding window: keys seen before the query's own; -1 = none
 };
 
 template <typename T, int D>
@@ -140,6 +141,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams a) {
     const int kv_len = im[M_KVLEN];
     const int t0 = pb * P;
     const int t1 = min(pe * P, kv_len);
+    // first key inside the window (keys before it in the first page are masked)
+    const int klo = a.window >= 0 && kv_len - 1 > a.window ? kv_len - 1 - a.window : 0;
     const int qrow = im[M_QOBASE];
     const int nch = t1 > t0 ? (t1 - t0 + kChunk - 1) / kChunk : 0;
 
@@ -223,6 +226,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams a) {
       if (cs + kChunk > t1) {  // tail chunk
 #pragma unroll
         for (int r = 0; r < 4; ++r) x[r] = (cs + 4 * kq + r < t1) ? x[r] : neg_inf();
+      }
+      if (cs < klo) {  // chunk starts before the window
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = (cs + 4 * kq + r >= klo) ? x[r] : neg_inf();
       }
       float cm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       cm = fmaxf(cm, __shfl_xor(cm, 16));
@@ -435,13 +442,16 @@ void decode_mfma_kernel(DecodeParams a) {
     }
     return r;
   };
-  // item geometry: keys [t0, t1), chunks of kChunk keys, the request's page ids at kvb
+  // item geometry: keys [t0, t1), chunks of kChunk keys, the request's page
+  // ids at kvb, and the first key inside the window (keys before it in the
+  // item's first page are masked)
   struct Ctx {
-    int t0, t1, kvb, nch;
+    int t0, t1, kvb, nch, klo;
   };
   auto make_ctx = [&](const Rec& r) -> Ctx {
     const int t0 = r.pb * P, t1 = min(r.pe * P, r.kv_len);
-    return Ctx{t0, t1, r.kvb, t1 > t0 ? (t1 - t0 + kChunk - 1) / kChunk : 0};
+    const int klo = a.window >= 0 && r.kv_len - 1 > a.window ? r.kv_len - 1 - a.window : 0;
+    return Ctx{t0, t1, r.kvb, t1 > t0 ? (t1 - t0 + kChunk - 1) / kChunk : 0, klo};
   };
   // page id of the wave's chunk 64 batch + lane, loaded raw (checked where
   // it is read, so the load is not waited for on the spot)
@@ -540,6 +550,10 @@ void decode_mfma_kernel(DecodeParams a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) x[r] = (cs + 4 * kq + r < t1) ? x[r] : neg_inf();
       }
+      if (cs < cx.klo) {  // chunk starts before the window
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = (cs + 4 * kq + r >= cx.klo) ? x[r] : neg_inf();
+      }
       const float cm = head_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
       const float m_new = cm > m_run + kMaxSlack ? cm : m_run;
       const float m_use = m_new == neg_inf() ? 0.f : m_new;
@@ -572,7 +586,7 @@ void decode_mfma_kernel(DecodeParams a) {
     };
 
     const bool has_next = it + 1 < it_end;
-    Ctx nx{0, 0, 0, 0};
+    Ctx nx{0, 0, 0, 0, 0};
     int pid_next = 0;
     {
       if (myn > 0 && !pre_issued) issue_k(wave, 0, 0, kA);
@@ -726,6 +740,7 @@ int launch_decode(const RunArgs& r) {
   p.scale_log2 = r.sm_scale * kLog2e;
   p.cap = r.soft_cap;
   p.inv_cap = r.soft_cap > 0.f ? 1.f / r.soft_cap : 0.f;
+  p.window = r.window;
   if (r.dtype == FI_BF16 && r.out_dtype == FI_BF16) return launch_d<BF16, BF16>(r, p);
   if (r.dtype == FI_BF16 && r.out_dtype == FI_F32) return launch_d<BF16, F32>(r, p);
   if (r.dtype == FI_F32 && r.out_dtype == FI_F32) return launch_d<F32, F32>(r, p);

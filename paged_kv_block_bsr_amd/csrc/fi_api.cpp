@@ -56,6 +56,7 @@ int check_plan(const int32_t* ph, const fi_attn_params* p, const char* who) {
       ph[H_PAGE] != p->page_size)
     return set_error(FI_ERR_PLAN_MISMATCH, "%s: plan built for other heads / head_dim / page_size",
                      who);
+  if (ph[H_WINDOW] < -1) return set_error(FI_ERR_PLAN_MISMATCH, "%s: corrupted window", who);
   for (int at : {(int)H_STREAM0, (int)H_STREAM1}) {
     const int32_t* sd = ph + at;
     if (sd[S_W] < 1 || sd[S_NSPLIT] > sd[S_W] - 1 || sd[S_NSLOTS] > sd[S_SLOTCAP])
@@ -91,6 +92,7 @@ RunArgs base_args(const int32_t* plan_dev, const fi_attn_params* p, const void* 
   a.P = p->page_size;
   a.G = a.Hq / a.Hk;
   a.causal = ph[H_CAUSAL];
+  a.window = ph[H_WINDOW];
   a.sm_scale = resolve_scale(p);
   a.soft_cap = p->logits_soft_cap;
   a.dtype = p->dtype;
@@ -243,6 +245,8 @@ int fi_cascade(const int32_t* plan0_host, const int32_t* plan0_dev, const int32_
   if ((rc = check_plan(plan1_host, params, "fi_cascade level 1"))) return rc;
   if (plan0_host[H_CAUSAL] != 0)
     return set_error(FI_ERR_PLAN_MISMATCH, "fi_cascade: level-0 plan must be non-causal");
+  if (plan0_host[H_WINDOW] >= 0 || plan1_host[H_WINDOW] >= 0)
+    return set_error(FI_ERR_UNSUPPORTED, "fi_cascade: plans with a sliding window are not supported");
   if (plan0_host[H_TOTAL_QO] != plan1_host[H_TOTAL_QO])
     return set_error(FI_ERR_PLAN_MISMATCH, "fi_cascade: levels cover different query rows");
   if (plan0_host[H_BATCH] > 0 && !qo_indptr0)

@@ -33,6 +33,7 @@ struct RunArgs {
   float* ws;                    // float workspace base
   int32_t Hq, Hk, D, P, G;
   int32_t causal;
+  int32_t window;               // sliding window (keys before the query's own); -1 = none
   float sm_scale;
   float soft_cap;
   fi_dtype dtype, out_dtype;

@@ -35,6 +35,7 @@ inline int64_t align64(int64_t n) { return ceil_div(n, 64) * 64; }
 
 struct Row {
   int32_t req, rb, re, vis;
+  int32_t fp;  // first visible page (not part of the rows array)
 };
 
 struct StreamPlan {
@@ -132,6 +133,7 @@ int validate(const fi_plan_in& in) {
       in.br_override != 64 && in.br_override != 128)
     return set_error(FI_ERR_INVALID_ARG, "fi_plan: br_override must be 0, 16, 32, 64 or 128");
   if (in.no_split != 0 && in.no_split != 1) return set_error(FI_ERR_INVALID_ARG, "fi_plan: no_split");
+  if (in.window_left < -1) return set_error(FI_ERR_INVALID_ARG, "fi_plan: window_left < -1");
   if (B > 0 && (!in.kv_indptr || !in.kv_last_page_len))
     return set_error(FI_ERR_INVALID_ARG, "fi_plan: null index array");
   if (B == 0 && !in.kv_indptr) return set_error(FI_ERR_INVALID_ARG, "fi_plan: null kv_indptr");
@@ -151,6 +153,8 @@ int validate(const fi_plan_in& in) {
     if (in.causal && qo >= 2 && qo > kv)
       return set_error(FI_ERR_INVALID_ARG, "fi_plan: causal request %d has qo_len %lld > kv_len %lld",
                        i, (long long)qo, (long long)kv);
+    if (in.window_left >= 0 && kv + qo >= kWindowMaxTokens)
+      return set_error(FI_ERR_UNSUPPORTED, "fi_plan: windowed request %d has kv_len + qo_len >= 2^30", i);
   }
   return FI_OK;
 }
@@ -227,16 +231,26 @@ int build_plan(const fi_plan_in* inp, int32_t* buf, int64_t capacity, fi_plan_in
   st[0].tile = G;
   st[1].W = in.workers_prefill;
   st[1].tile = BR;
+  // A row of query tokens [tok_lo, tok_hi] sees keys [first, end): end from
+  // the causal bound of tok_hi (or kv_len), first from the window bound of
+  // tok_lo (or 0); its pages are first / P .. ceil(end / P).
+  const int64_t w = in.window_left;
+  auto first_page = [&](int i, int64_t tok_lo) -> int64_t {
+    return w < 0 ? 0 : std::max<int64_t>(0, kv[i] - qo[i] + tok_lo - w) / P;
+  };
   for (int i = 0; i < B; ++i) {
     if (qo[i] == 1) {
-      st[0].rows.push_back({i, 0, G, (int32_t)np[i]});
+      const int64_t fp = first_page(i, 0);
+      st[0].rows.push_back({i, 0, G, (int32_t)std::max<int64_t>(0, np[i] - fp), (int32_t)fp});
     } else if (qo[i] >= 2) {
       const int64_t npk = qo[i] * G;
       for (int64_t rb = 0; rb < npk; rb += BR) {
         int64_t re = std::min<int64_t>(rb + BR, npk);
         int64_t tok_hi = (re - 1) / G;
-        int64_t vis = in.causal ? kv[i] - qo[i] + tok_hi + 1 : kv[i];
-        st[1].rows.push_back({i, (int32_t)rb, (int32_t)re, (int32_t)ceil_div(vis, P)});
+        int64_t end = in.causal ? kv[i] - qo[i] + tok_hi + 1 : kv[i];
+        const int64_t fp = first_page(i, rb / G);
+        st[1].rows.push_back({i, (int32_t)rb, (int32_t)re,
+                              (int32_t)std::max<int64_t>(0, ceil_div(end, P) - fp), (int32_t)fp});
       }
     }
   }
@@ -282,10 +296,11 @@ int build_plan(const fi_plan_in* inp, int32_t* buf, int64_t capacity, fi_plan_in
       buf[pos++] = r.vis;
     }
     d[S_OFF_ITEMS] = (int32_t)pos;
-    for (int64_t j = 0; j < ni; ++j) {
+    for (int64_t j = 0; j < ni; ++j) {  // request pages: shifted by the row's first visible page
+      const int32_t fp = s.rows[s.item_row[j]].fp;
       buf[pos++] = s.item_row[j];
-      buf[pos++] = s.item_pb[j];
-      buf[pos++] = s.item_pe[j];
+      buf[pos++] = fp + s.item_pb[j];
+      buf[pos++] = fp + s.item_pe[j];
       buf[pos++] = s.item_slot[j];
     }
     d[S_OFF_WIP] = (int32_t)pos;
@@ -319,6 +334,7 @@ int build_plan(const fi_plan_in* inp, int32_t* buf, int64_t capacity, fi_plan_in
   buf[H_CAUSAL] = in.causal ? 1 : 0;
   buf[H_GROUP] = G;
   buf[H_WS_FLOATS] = (int32_t)ws_total;
+  buf[H_WINDOW] = in.window_left;
   if (info) {
     info->plan_ints = pos;
     info->float_ws_bytes = ws_total * 4;

@@ -4,6 +4,7 @@
 // The buffer starts with a fixed header, then per stream (0 = decode rows,
 // 1 = prefill tiles) five arrays:
 //   rows   [n_rows][4]  {request, packed_row_begin, packed_row_end, visible_pages}
+//                        (counted from the row's first visible page)
 //   items  [n_items][4] {row, page_begin, page_end, slot}  (slot -1: write the
 //                        output directly; else the partial-result slot)
 //   wip    [W+1]        items of worker w are items[wip[w] .. wip[w+1])
@@ -14,9 +15,14 @@
 //                        request and row (qo_base = qo_indptr[request], or the
 //                        request itself for a decode-only batch), so a kernel
 //                        reads one record per item instead of a dependent chain
+// A row's first visible page is 0, or, with a sliding window of w keys
+// (header word H_WINDOW >= 0), the page of key max(0, kv_len - qo_len +
+// tok_lo - w), tok_lo being the row's first query token: no query of the row
+// sees a key before it.
 // A packed row r of a request stands for (token r / G, head-in-group r % G);
 // a decode row packs the G query heads of one KV head.  Page indices in
-// items are local to the request (the kernel adds kv_indptr[request]).
+// items are local to the request (the kernel adds kv_indptr[request]); a
+// row's items cover its pages [first, first + visible_pages).
 //
 // The float workspace holds, per stream, partial outputs [slot_cap][Hk][tile][D]
 // and partial lse [slot_cap][Hk][tile] (fp32, natural log) at the float offsets
@@ -27,12 +33,15 @@
 namespace fi {
 
 constexpr int32_t kPlanMagic = 0x31504946;  // "FIP1"
-constexpr int32_t kPlanVersion = 1;
+constexpr int32_t kPlanVersion = 2;
 constexpr int kHeaderInts = 64;
 constexpr int kMetaInts = 8;  // ints per item_meta record
 // item_meta fields
 enum : int { M_REQ = 0, M_KVB = 1, M_KVLEN = 2, M_QOBASE = 3, M_QOLEN = 4, M_RB = 5, M_RE = 6 };
 constexpr int kMaxTileRows = 128;
+// A request of a windowed plan needs kv_len + qo_len below this, so that the
+// kernels' key bounds stay inside int32.
+constexpr int64_t kWindowMaxTokens = (int64_t)1 << 30;
 
 // header words
 enum : int {
@@ -50,6 +59,7 @@ enum : int {
   H_WS_FLOATS = 11,
   H_STREAM0 = 12,
   H_STREAM1 = 32,
+  H_WINDOW = 52,  // sliding window: keys a query sees before its own; -1 = none
 };
 
 // stream descriptor words (relative to H_STREAM0 / H_STREAM1)

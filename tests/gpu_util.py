@@ -46,7 +46,8 @@ def plan_for(b, workers_decode, workers_prefill=1, min_seg_pages=8, no_split=0, 
                       num_qo_heads=b.num_qo_heads, num_kv_heads=b.num_kv_heads,
                       head_dim=b.head_dim, causal=b.causal, workers_decode=workers_decode,
                       workers_prefill=workers_prefill, min_seg_pages=min_seg_pages,
-                      br_override=br_override, no_split=no_split)
+                      br_override=br_override, no_split=no_split,
+                      window_left=getattr(b, "window_left", -1))
 
 
 def run(b, workers_decode=None, workers_prefill=None, min_seg_pages=8, no_split=0,

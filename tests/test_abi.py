@@ -81,7 +81,8 @@ def test_fi_plan_bit_exact_vs_oracle_random(seed):
              num_qo_heads=Hk * G, num_kv_heads=Hk, head_dim=int(rng.choice([64, 128])),
              causal=causal, workers_decode=int(rng.integers(1, 40)),
              workers_prefill=int(rng.integers(1, 40)), min_seg_pages=int(rng.integers(1, 10)),
-             br_override=int(rng.choice([0, 0, 16, 64])), no_split=int(rng.integers(0, 2)))
+             br_override=int(rng.choice([0, 0, 16, 64])), no_split=int(rng.integers(0, 2)),
+             window_left=int(rng.choice([-1, -1, 0, 3, 50, 400])))
 
 
 @pytest.mark.parametrize("name", ["tiny_decode_fp32", "llama8b_decode", "skewed_long_decode",
@@ -123,6 +124,9 @@ def test_fi_plan_bit_exact_on_named_workloads(name, monkeypatch):
     (dict(kv_indptr=[0, 2, 1]), fi.binding.FI_ERR_INVALID_ARG),
     (dict(qo_indptr=[0, 9, 10]), fi.binding.FI_ERR_INVALID_ARG),
     (dict(qo_indptr=[0, 2, 1]), fi.binding.FI_ERR_INVALID_ARG),
+    (dict(window_left=-2), fi.binding.FI_ERR_INVALID_ARG),
+    (dict(qo_indptr=[0, 2, 3], kv_indptr=[0, 2 ** 28, 2 ** 28 + 1],
+          kv_last_page_len=[4, 3], window_left=5), fi.binding.FI_ERR_UNSUPPORTED),
 ])
 def test_fi_plan_error_codes_match_oracle(bad, code):
     kw = dict(qo_indptr=[0, 2, 3], kv_indptr=[0, 2, 3], kv_last_page_len=[4, 3], page_size=4,
@@ -179,6 +183,18 @@ def test_run_calls_reject_bad_arguments_without_a_gpu():
     rc = L.fi_batch_decode_paged(bad.ctypes.data, 16, ctypes.byref(params), 16, 16, 10, 16, 16, 16,
                                  16, None, 16, 1 << 20, None)
     assert rc == fi.binding.FI_ERR_PLAN_MISMATCH
+
+
+def test_cascade_rejects_windowed_plans_without_a_gpu():
+    torch = __import__("torch")
+    kw = dict(page_size=16, num_qo_heads=8, num_kv_heads=2, head_dim=128, workers_decode=2,
+              workers_prefill=2, window_left=8)
+    p0 = fi.fi_plan([0, 1], [0, 2], [3], causal=False, **kw)
+    p1 = fi.fi_plan([0, 1], [0, 1], [5], causal=True, **kw)
+    params = fi.make_params(torch.bfloat16, torch.bfloat16, 8, 2, 128, 16)
+    rc = fi.lib().fi_cascade(p0.host_ptr(), 16, 16, 16, 16, 16, p1.host_ptr(), 16, 16, 16, 16, 16,
+                             ctypes.byref(params), 16, 16, 10, 16, None, 16, 1 << 24, None)
+    assert rc == fi.binding.FI_ERR_UNSUPPORTED and "window" in fi.fi_last_error()
 
 
 def test_append_rejects_bad_arguments():

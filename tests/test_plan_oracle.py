@@ -64,9 +64,11 @@ def _check_stream(st, no_split):
         owner[wip[w]:wip[w + 1]] = w
         rs = [items[k][0] for k in range(wip[w], wip[w + 1])]
         assert rs == sorted(rs)
+    fps = st["first_page"]
     per_row = {r: [] for r in range(len(rows))}
     for k, (r, pb, pe, slot) in enumerate(items):
-        per_row[r].append((pb, pe, slot, owner[k]))
+        # item pages are request pages; relative to the row's first page here
+        per_row[r].append((pb - fps[r], pe - fps[r], slot, owner[k]))
     mi = st["merge_indptr"]
     assert len(mi) == len(rows) + 1 and mi[0] == 0
     for r, lst in per_row.items():
@@ -97,7 +99,7 @@ def _check_stream(st, no_split):
         assert st["merge_indptr"][-1] <= 2 * (W - 1)
         assert S == max(st["min_seg"], -(-sum(vis) // W))
         bf = brute_force_items(vis, W, S)
-        got = sorted([(owner[k], r, pb, pe) for k, (r, pb, pe, slot) in enumerate(items)],
+        got = sorted([(owner[k], r, pb - fps[r], pe - fps[r]) for k, (r, pb, pe, slot) in enumerate(items)],
                      key=lambda t: (t[0], t[1]))
         assert got == bf
 
@@ -185,6 +187,9 @@ def test_long_request_is_split_into_equal_segments():
     (dict(kv_indptr=[0, 2, 1]), pr.FI_ERR_INVALID_ARG),
     (dict(qo_indptr=[0, 9, 10]), pr.FI_ERR_INVALID_ARG),
     (dict(qo_indptr=[0, 2, 1]), pr.FI_ERR_INVALID_ARG),
+    (dict(window_left=-2), pr.FI_ERR_INVALID_ARG),
+    (dict(qo_indptr=[0, 2, 3], kv_indptr=[0, 2 ** 28, 2 ** 28 + 1],
+          kv_last_page_len=[4, 3], window_left=5), pr.FI_ERR_UNSUPPORTED),
 ])
 def test_plan_oracle_validation(bad, code):
     kw = dict(qo_indptr=[0, 2, 3], kv_indptr=[0, 2, 3], kv_last_page_len=[4, 3], page_size=4,
@@ -245,3 +250,82 @@ def test_item_meta_describes_each_items_request_and_row(seed):
                 assert m == (req, kv_indptr[req], want_kv, want_qb, want_ql, rb, re, 0)
             off = st["off_item_meta"]
             assert res["buf"][off:off + 8 * len(st["item_meta"])] == [x for m in st["item_meta"] for x in m]
+
+
+def _visible_pages(kv, qo, toks, P, causal, window):
+    """Pages holding a key that some query token of ``toks`` sees, straight
+    from the definition: token t (position p = kv - qo + t) sees key j iff
+    j < kv, j <= p when causal, and j >= p - window when window >= 0."""
+    pages = set()
+    for t in toks:
+        p = kv - qo + t
+        for j in range(kv):
+            if causal and j > p:
+                continue
+            if window >= 0 and j < p - window:
+                continue
+            pages.add(j // P)
+    return pages
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_window_rows_cover_exactly_the_pages_their_queries_see(seed):
+    """With a sliding window every row's items cover exactly the pages that
+    hold a key one of its queries sees (a brute-force visibility map), and
+    the partition invariants still hold."""
+    rng = np.random.default_rng(3000 + seed)
+    P = int(rng.choice([1, 3, 16]))
+    causal = bool(rng.integers(0, 2))
+    B = int(rng.integers(1, 8))
+    qo_indptr, kv_indptr, last, qo, kv = _random_case(rng, B, 24, 160, P, causal)
+    window = int(rng.choice([0, 1, 5, 17, 40, 100, 1000]))
+    G = int(rng.choice([1, 2, 4]))
+    ms = int(rng.integers(1, 4))
+    no_split = int(rng.integers(0, 2))
+    code, res = pr.plan(qo_indptr, kv_indptr, last, page_size=P, num_qo_heads=2 * G,
+                        num_kv_heads=2, head_dim=64, causal=causal, workers_decode=int(rng.integers(1, 9)),
+                        workers_prefill=int(rng.integers(1, 9)), min_seg_pages=ms,
+                        no_split=no_split, window_left=window)
+    assert code == 0, res
+    assert res["buf"][pr.WINDOW_AT] == window
+    for st in (res["decode"], res["prefill"]):
+        st["min_seg"] = ms
+        _check_stream(st, no_split)
+        covered = {r: set() for r in range(len(st["rows"]))}
+        for (r, pb, pe, slot) in st["items"]:
+            covered[r] |= set(range(pb, pe))
+        for r, (i, rb, re, vp) in enumerate(st["rows"]):
+            toks = range(rb // G, (re - 1) // G + 1)
+            want = _visible_pages(int(kv[i]), int(qo[i]), toks, P, causal, window)
+            assert covered[r] == want, (r, i, rb, re)
+            assert vp == len(want)
+
+
+def test_window_as_long_as_every_request_changes_no_array():
+    rng = np.random.default_rng(3100)
+    qo_indptr, kv_indptr, last, qo, kv = _random_case(rng, 10, 30, 300, 16, True)
+    kw = dict(page_size=16, num_qo_heads=8, num_kv_heads=2, head_dim=128, causal=True,
+              workers_decode=7, workers_prefill=5, min_seg_pages=2)
+    _, none = pr.plan(qo_indptr, kv_indptr, last, **kw)
+    _, wide = pr.plan(qo_indptr, kv_indptr, last, window_left=int(kv.max()), **kw)
+    assert none["buf"][pr.WINDOW_AT] == -1 and wide["buf"][pr.WINDOW_AT] == int(kv.max())
+    a, b = list(none["buf"]), list(wide["buf"])
+    a[pr.WINDOW_AT] = b[pr.WINDOW_AT] = 0
+    assert a == b
+
+
+def test_window_zero_decode_rows_keep_only_the_last_page():
+    # a window of 0 keys: a decode query sees its own key alone, the last one
+    kv = np.array([1, 16, 17, 100, 0])
+    npg = -(-kv // 16)
+    kv_indptr = np.concatenate([[0], np.cumsum(npg)])
+    last = np.where(npg > 0, kv - (npg - 1) * 16, 0)
+    code, res = pr.plan(None, kv_indptr, last, page_size=16, num_qo_heads=4, num_kv_heads=1,
+                        head_dim=64, causal=True, workers_decode=3, workers_prefill=1,
+                        window_left=0)
+    assert code == 0
+    st = res["decode"]
+    assert [r[3] for r in st["rows"]] == [1, 1, 1, 1, 0]
+    for (r, pb, pe, slot) in st["items"]:
+        n = int(npg[r])
+        assert (pb, pe) == ((n - 1, n) if n else (0, 0))

@@ -60,6 +60,7 @@ class PagedBatch:
     kv_pool: torch.Tensor          # [pool_pages, 2, P, Hk, D]
     name: str = ""
     meta: dict = field(default_factory=dict)
+    window_left: int = -1          # sliding window (keys before the query's own); -1 = none
 
     @property
     def batch_size(self) -> int:
@@ -144,15 +145,17 @@ def make_batch(seed: int, qo_lens, kv_lens, *, page_size=16, num_qo_heads=32,
                num_kv_heads=8, head_dim=128, dtype=torch.bfloat16, causal=True,
                decode=False, pool_factor=1.25, pool_pages=None, soft_cap=0.0,
                sm_scale=None, nan_poison=False, identity_pages=False,
-               name="") -> PagedBatch:
+               name="", window_left=-1) -> PagedBatch:
     """Generic seeded batch.  ``decode=True`` means qo_indptr is None and every
     request has exactly one query token."""
     rng = np.random.default_rng(seed)
     kv_lens = np.asarray(kv_lens, dtype=np.int64)
     qo_lens = np.ones_like(kv_lens) if decode else np.asarray(qo_lens, dtype=np.int64)
-    return _assemble(rng, qo_lens, kv_lens, page_size, num_qo_heads, num_kv_heads,
-                     head_dim, dtype, causal, decode, pool_factor, pool_pages,
-                     soft_cap, sm_scale, nan_poison, identity_pages, name)
+    b = _assemble(rng, qo_lens, kv_lens, page_size, num_qo_heads, num_kv_heads,
+                  head_dim, dtype, causal, decode, pool_factor, pool_pages,
+                  soft_cap, sm_scale, nan_poison, identity_pages, name)
+    b.window_left = int(window_left)
+    return b
 
 
 def _assemble(rng, qo_lens, kv_lens, P, Hq, Hk, D, dtype, causal, decode,
