@@ -43,13 +43,14 @@ def lib():
             L.oref_attention_rows.restype = ctypes.c_int
             L.oref_attention_rows.argtypes = [
                 ctypes.c_int, _i32p, _i32p, _i32p, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_int, _f64p,
-                _f64p, ctypes.c_int64, ctypes.c_int64, _i32p, _i32p, _i32p, _f64p, _f64p]
+                ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_int,
+                ctypes.c_double, ctypes.c_double, _f64p, _f64p, ctypes.c_int64, ctypes.c_int64,
+                _i32p, _i32p, _i32p, _f64p, _f64p]
             L.oref_attention.restype = ctypes.c_int
             L.oref_attention.argtypes = [
                 ctypes.c_int, _i32p, _i32p, _i32p, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_int, _f64p,
-                _f64p, ctypes.c_int64, _f64p, _f64p]
+                ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_int,
+                ctypes.c_double, ctypes.c_double, _f64p, _f64p, ctypes.c_int64, _f64p, _f64p]
             L.oref_merge_states.restype = ctypes.c_int
             L.oref_merge_states.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, _f64p,
                                             _f64p, _f64p, _f64p]
@@ -109,14 +110,16 @@ def token_location(kv_indptr, kv_indices, page_size, request, token):
 
 def attention(q, kv_pool, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, *, page_size,
               num_qo_heads, num_kv_heads, head_dim, causal, sm_scale, soft_cap=0.0,
-              window_left=-1):
+              window_left=-1, rope_theta=0.0, rope_scale=1.0):
     """Exact attention for every query row.
 
     q: [total_qo, Hq, D]; kv_pool: [pages, 2, P, Hk, D]; qo_indptr None means
     one query per request.  Returns (o [total_qo, Hq, D], lse [total_qo, Hq]),
     float64, lse in natural log (-inf where no key is visible).  window_left
     >= 0: the query at position kv_len - qo_len + t sees no key more than
-    window_left positions before it.
+    window_left positions before it.  rope_theta > 0: rotary embedding of q
+    (at position kv_len - qo_len + t) and k (at position j), rotate-half form
+    with angle pos / rope_scale * rope_theta^(-2d/D).
     """
     B = len(kv_indptr) - 1
     qa, q_p = _f64(q)
@@ -130,7 +133,7 @@ def attention(q, kv_pool, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, *,
     lse = np.zeros((total, num_qo_heads), np.float64)
     _check(lib().oref_attention(B, qo_p, kp_p, ki_p, kl_p, page_size, num_qo_heads, num_kv_heads,
                                 head_dim, int(causal), float(sm_scale), float(soft_cap),
-                                int(window_left), q_p, p_p,
+                                int(window_left), float(rope_theta), float(rope_scale), q_p, p_p,
                                 int(pa.shape[0]), o.ctypes.data_as(_f64p),
                                 lse.ctypes.data_as(_f64p)))
     return o, lse
@@ -138,7 +141,7 @@ def attention(q, kv_pool, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, *,
 
 def attention_rows(q, kv_pool, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, rows, *,
                    page_size, num_qo_heads, num_kv_heads, head_dim, causal, sm_scale,
-                   soft_cap=0.0, window_left=-1):
+                   soft_cap=0.0, window_left=-1, rope_theta=0.0, rope_scale=1.0):
     """Exact attention for selected rows.  ``rows`` is an int array [n, 3] of
     (request, token-in-request, query head).  Returns (o [n, D], lse [n])."""
     B = len(kv_indptr) - 1
@@ -157,7 +160,8 @@ def attention_rows(q, kv_pool, qo_indptr, kv_indptr, kv_indices, kv_last_page_le
     lse = np.zeros((n,), np.float64)
     _check(lib().oref_attention_rows(B, qo_p, kp_p, ki_p, kl_p, page_size, num_qo_heads,
                                      num_kv_heads, head_dim, int(causal), float(sm_scale),
-                                     float(soft_cap), int(window_left), q_p, p_p, int(pa.shape[0]), n,
+                                     float(soft_cap), int(window_left), float(rope_theta),
+                                     float(rope_scale), q_p, p_p, int(pa.shape[0]), n,
                                      rq_p, rt_p,
                                      rh_p, o.ctypes.data_as(_f64p), lse.ctypes.data_as(_f64p)))
     return o, lse
@@ -186,7 +190,8 @@ def attention_of(batch, **overrides):
     kw = dict(page_size=batch.page_size, num_qo_heads=batch.num_qo_heads,
               num_kv_heads=batch.num_kv_heads, head_dim=batch.head_dim, causal=batch.causal,
               sm_scale=batch.sm_scale, soft_cap=batch.soft_cap,
-              window_left=getattr(batch, "window_left", -1))
+              window_left=getattr(batch, "window_left", -1),
+              rope_theta=getattr(batch, "rope_theta", 0.0), rope_scale=getattr(batch, "rope_scale", 1.0))
     kw.update(overrides)
     return attention(batch.q, batch.kv_pool, batch.qo_indptr, batch.kv_indptr, batch.kv_indices,
                      batch.kv_last_page_len, **kw)
@@ -196,7 +201,8 @@ def attention_rows_of(batch, rows, **overrides):
     kw = dict(page_size=batch.page_size, num_qo_heads=batch.num_qo_heads,
               num_kv_heads=batch.num_kv_heads, head_dim=batch.head_dim, causal=batch.causal,
               sm_scale=batch.sm_scale, soft_cap=batch.soft_cap,
-              window_left=getattr(batch, "window_left", -1))
+              window_left=getattr(batch, "window_left", -1),
+              rope_theta=getattr(batch, "rope_theta", 0.0), rope_scale=getattr(batch, "rope_scale", 1.0))
     kw.update(overrides)
     return attention_rows(batch.q, batch.kv_pool, batch.qo_indptr, batch.kv_indptr,
                           batch.kv_indices, batch.kv_last_page_len, rows, **kw)

@@ -38,6 +38,15 @@
  *     with window_left >= 0 the query at position kv_len - qo_len + t sees no
  *     key more than window_left positions before it (window_left < 0: no
  *     window).
+ *   - fused rotary embedding (paper page, opening paragraph: fused rotary
+ *     embeddings among the attention variants; "Customizable attention": a
+ *     query / key transform such as RoPE): with rope_theta > 0, q and k are
+ *     rotated before the dot product, v is not.  The pages give no formula;
+ *     the reading is the rotate-half form: for d < D/2 the pair
+ *     (x[d], x[d + D/2]) turns by the angle (pos / rope_scale) *
+ *     rope_theta^(-2d/D), where the key j of a request sits at position j and
+ *     the query t at kv_len - qo_len + t (the same alignment as the causal
+ *     mask).  rope_scale <= 0 means 1.
  *
  * Parity pins: see the oracle tests (dense brute force, library SDPA, closed
  * forms, the pages' page-table example, page-permutation invariance,
@@ -131,6 +140,22 @@ int oref_token_location(const int32_t *kv_indptr, const int32_t *kv_indices, int
   return OREF_OK;
 }
 
+/*
+ * Rotary embedding of one head vector x (length D, even) at position pos:
+ * for d < D/2 the pair (x[d], x[d + D/2]) is rotated by the angle
+ * pos / scale * theta^(-2d/D).  Writes y; x and y do not overlap.
+ */
+static void rope_rotate(const double *x, double *y, int D, double pos, double theta,
+                        double scale) {
+  const int h = D / 2;
+  for (int d = 0; d < h; ++d) {
+    const double ang = pos / scale * pow(theta, -2.0 * d / D);
+    const double c = cos(ang), s = sin(ang);
+    y[d] = x[d] * c - x[d + h] * s;
+    y[d + h] = x[d + h] * c + x[d] * s;
+  }
+}
+
 /* Element (page, kv, slot, head, d) of the pool [pages, 2, P, Hk, D]. */
 static inline double pool_at(const double *pool, int64_t page, int kv, int64_t slot, int g,
                              int d, int P, int Hk, int D) {
@@ -144,12 +169,16 @@ static inline double pool_at(const double *pool, int64_t page, int kv, int64_t s
 int oref_attention_rows(int B, const int32_t *qo_indptr, const int32_t *kv_indptr,
                         const int32_t *kv_indices, const int32_t *kv_last_page_len, int P,
                         int Hq, int Hk, int D, int causal, double sm_scale, double soft_cap,
-                        int window_left, const double *q, const double *pool, int64_t pool_pages,
+                        int window_left, double rope_theta, double rope_scale,
+                        const double *q, const double *pool, int64_t pool_pages,
                         int64_t n_rows, const int32_t *row_req, const int32_t *row_tok,
                         const int32_t *row_head, double *o, double *lse) {
   int rc = oref_validate(B, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, P, Hq, Hk, D,
                          causal, pool_pages);
   if (rc) return rc;
+  const int rope = rope_theta > 0.0;
+  if (rope && D % 2) return fail("rotary embedding needs an even head_dim", D, 0);
+  if (rope_scale <= 0.0) rope_scale = 1.0;
   for (int64_t r = 0; r < n_rows; ++r) {
     int i = row_req[r];
     if (i < 0 || i >= B) return fail("row request out of range", r, i);
@@ -179,18 +208,28 @@ int oref_attention_rows(int B, const int32_t *qo_indptr, const int32_t *kv_indpt
       continue;
     }
     double *s = (double *)malloc(sizeof(double) * (size_t)(limit - first));
-    if (!s) {
+    double *qrot = (double *)malloc(sizeof(double) * (size_t)D * 3);
+    if (!s || !qrot) {
+      free(s);
+      free(qrot);
 #pragma omp critical
       rc_all = OREF_ENOMEM;
       continue;
     }
+    /* rotary embedding: the query at its position, each key at its own */
+    double *kraw = qrot + D, *krot = qrot + 2 * D;
+    if (rope) rope_rotate(qrow, qrot, D, (double)(kv_len - qo_len + t), rope_theta, rope_scale);
+    const double *qv = rope ? qrot : qrow;
     /* pass 1: logits of every visible key, gathered one token at a time */
     double m = -INFINITY;
     for (int64_t j = first; j < limit; ++j) {
       int64_t page = kv_indices[kv_indptr[i] + j / P];
       int64_t slot = j % P;
+      for (int d = 0; d < D; ++d) kraw[d] = pool_at(pool, page, 0, slot, g, d, P, Hk, D);
+      if (rope) rope_rotate(kraw, krot, D, (double)j, rope_theta, rope_scale);
+      const double *kv = rope ? krot : kraw;
       double acc = 0.0;
-      for (int d = 0; d < D; ++d) acc += qrow[d] * pool_at(pool, page, 0, slot, g, d, P, Hk, D);
+      for (int d = 0; d < D; ++d) acc += qv[d] * kv[d];
       acc *= sm_scale;
       if (soft_cap > 0.0) acc = soft_cap * tanh(acc / soft_cap);
       s[j - first] = acc;
@@ -209,6 +248,7 @@ int oref_attention_rows(int B, const int32_t *qo_indptr, const int32_t *kv_indpt
     for (int d = 0; d < D; ++d) orow[d] /= z;
     lse[r] = m + log(z);
     free(s);
+    free(qrot);
   }
   return rc_all;
 }
@@ -219,7 +259,8 @@ int oref_attention_rows(int B, const int32_t *qo_indptr, const int32_t *kv_indpt
 int oref_attention(int B, const int32_t *qo_indptr, const int32_t *kv_indptr,
                    const int32_t *kv_indices, const int32_t *kv_last_page_len, int P, int Hq,
                    int Hk, int D, int causal, double sm_scale, double soft_cap, int window_left,
-                   const double *q, const double *pool, int64_t pool_pages, double *o, double *lse) {
+                   double rope_theta, double rope_scale, const double *q, const double *pool,
+                   int64_t pool_pages, double *o, double *lse) {
   int64_t total = 0;
   for (int i = 0; i < B; ++i) total += qo_len_of(qo_indptr, i);
   int64_t n = total * Hq;
@@ -237,7 +278,8 @@ int oref_attention(int B, const int32_t *qo_indptr, const int32_t *kv_indptr,
         rq[r] = i; rt[r] = (int32_t)t; rh[r] = h; ++r;
       }
   int rc = oref_attention_rows(B, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, P, Hq, Hk,
-                               D, causal, sm_scale, soft_cap, window_left, q, pool, pool_pages, n,
+                               D, causal, sm_scale, soft_cap, window_left, rope_theta, rope_scale,
+                               q, pool, pool_pages, n,
                                rq, rt, rh, o, lse);
   free(rq); free(rt); free(rh);
   return rc;

@@ -472,3 +472,113 @@ def test_window_equals_attention_over_the_visible_keys_alone(causal, cap):
                 o_s, l_s = ref.attention_of(sub)
                 assert np.allclose(o[qo[i] + t], o_s[0], rtol=0, atol=1e-12), (w, i, t)
                 assert np.allclose(lse[qo[i] + t], l_s[0], rtol=0, atol=1e-12), (w, i, t)
+
+
+# ---- rotary embedding (rotate-half reading: the pair (x[d], x[d + D/2])
+# turns by pos / scale * theta^(-2d/D); key j at position j, query t at
+# kv_len - qo_len + t)
+
+def _rope_pair_case(q, k0, k1, theta, scale):
+    """One decode request with two keys (positions 0 and 1), D = 4; the query
+    sits at position 1.  V = identity rows so o reads back the weights."""
+    P = 2
+    pool = np.zeros((1, 2, P, 1, 4))
+    pool[0, 0, 0, 0] = k0
+    pool[0, 0, 1, 0] = k1
+    pool[0, 1, 0, 0] = [1, 0, 0, 0]
+    pool[0, 1, 1, 0] = [0, 1, 0, 0]
+    qa = np.asarray(q, np.float64).reshape(1, 1, 4)
+    return ref.attention(qa, pool, None, np.array([0, 1], np.int32), np.array([0], np.int32),
+                         np.array([2], np.int32), page_size=P, num_qo_heads=1, num_kv_heads=1,
+                         head_dim=4, causal=True, sm_scale=1.0, rope_theta=theta, rope_scale=scale)
+
+
+@pytest.mark.parametrize("scale", [1.0, 2.0])
+def test_rope_closed_form_first_pair(scale):
+    # pair d = 0 turns by pos / scale rad: q = e0 at position 1 becomes
+    # (cos a, 0, sin a, 0); k0 = e0 at position 0 stays; k1 = e2 at
+    # position 1 becomes (-sin a, 0, cos a, 0).  Logits cos a and 0.
+    a = 1.0 / scale
+    o, lse = _rope_pair_case([1, 0, 0, 0], [1, 0, 0, 0], [0, 0, 1, 0], 100.0, scale)
+    s0, s1 = math.cos(a), 0.0
+    assert lse[0, 0] == pytest.approx(math.log(math.exp(s0) + math.exp(s1)), abs=1e-14)
+    w0 = math.exp(s0) / (math.exp(s0) + math.exp(s1))
+    assert o[0, 0, 0] == pytest.approx(w0, abs=1e-14) and o[0, 0, 1] == pytest.approx(1 - w0, abs=1e-14)
+
+
+@pytest.mark.parametrize("scale", [1.0, 2.0])
+def test_rope_closed_form_second_pair(scale):
+    # pair d = 1 of D = 4 turns by pos / scale * theta^(-1/2) = 0.1 / scale
+    # at theta 100: logits cos(0.1 / scale) (k0 = e1 at position 0) and 0
+    # (k1 = e3 at position 1).
+    a = 0.1 / scale
+    o, lse = _rope_pair_case([0, 1, 0, 0], [0, 1, 0, 0], [0, 0, 0, 1], 100.0, scale)
+    assert lse[0, 0] == pytest.approx(math.log(math.exp(math.cos(a)) + 1.0), abs=1e-14)
+
+
+def test_rope_at_position_zero_is_the_identity():
+    # one key, one query: both at position 0, so the logit (= lse) is the
+    # plain scaled dot product and o is the key's value
+    b = _window_batch(601, [1, 1], [1, 1], 4, True)
+    o0, l0 = ref.attention_of(b)
+    o1, l1 = ref.attention_of(b, rope_theta=10000.0)
+    assert np.allclose(l0, l1, atol=1e-14, rtol=0) and np.allclose(o0, o1, atol=1e-14, rtol=0)
+
+
+def _rotate_complex(x, pos, theta, scale):
+    """Independent form of the rotation: pair (x[d], x[d + D/2]) as the
+    complex number x[d] + i x[d + D/2], multiplied by exp(i angle)."""
+    D = x.shape[-1]
+    h = D // 2
+    ang = np.asarray(pos, np.float64)[..., None] / scale * theta ** (-2.0 * np.arange(h) / D)
+    z = (x[..., :h] + 1j * x[..., h:]) * np.exp(1j * ang)
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+@pytest.mark.parametrize("causal,theta,scale", [(True, 10000.0, 1.0), (False, 500.0, 4.0),
+                                                 (True, 1e6, 0.5)])
+def test_rope_equals_plain_attention_on_rotated_inputs(causal, theta, scale):
+    """Rotating q and every cached key up front (complex form, numpy) and
+    running plain attention gives the fused result: this pins the positions
+    (key j at j, query t at kv_len - qo_len + t) and the frequencies."""
+    b = _window_batch(602, [1, 6, 3], [37, 13, 3], 4, causal)
+    q = b.q.numpy().astype(np.float64)
+    pool = b.kv_pool.numpy().astype(np.float64).copy()
+    qr = q.copy()
+    for i in range(3):
+        kv = int(b.kv_lens[i])
+        q0, q1 = int(b.qo_indptr[i]), int(b.qo_indptr[i + 1])
+        qr[q0:q1] = _rotate_complex(q[q0:q1], (kv - (q1 - q0) + np.arange(q1 - q0))[:, None], theta, scale)
+        pages = b.kv_indices[b.kv_indptr[i]:b.kv_indptr[i + 1]]
+        for j in range(kv):
+            pg, sl = pages[j // 4], j % 4
+            pool[pg, 0, sl] = _rotate_complex(pool[pg, 0, sl], np.full(pool.shape[3], j), theta, scale)
+    o0, l0 = ref.attention(qr, pool, b.qo_indptr, b.kv_indptr, b.kv_indices, b.kv_last_page_len,
+                           page_size=4, num_qo_heads=4, num_kv_heads=2, head_dim=8, causal=causal,
+                           sm_scale=b.sm_scale)
+    o1, l1 = ref.attention_of(b, rope_theta=theta, rope_scale=scale)
+    assert np.allclose(o0, o1, atol=1e-12, rtol=0) and np.allclose(l0, l1, atol=1e-12, rtol=0)
+
+
+def test_rope_logits_depend_only_on_relative_positions():
+    """A request whose keys sit c positions later (c extra keys in front,
+    hidden by a window) gives the same output: rotary logits depend only
+    on position differences."""
+    import workloads as wl
+    c, L, w = 9, 20, 11
+    a = wl.make_batch(603, None, [L], page_size=1, num_qo_heads=4, num_kv_heads=2, head_dim=8,
+                      dtype=torch.float32, decode=True)
+    bb = wl.make_batch(604, None, [L + c], page_size=1, num_qo_heads=4, num_kv_heads=2, head_dim=8,
+                       dtype=torch.float32, decode=True)
+    pa, pb = a.kv_pool.numpy(), bb.kv_pool.numpy().copy()
+    for j in range(L):   # B's key c + j = A's key j (pages of one token each)
+        pb[bb.kv_indices[c + j]] = pa[a.kv_indices[j]]
+    bb.kv_pool = torch.from_numpy(pb)
+    bb.q = a.q.clone()
+    oa, la = ref.attention_of(a, window_left=w, rope_theta=10000.0)
+    ob, lb = ref.attention_of(bb, window_left=w, rope_theta=10000.0)
+    assert np.allclose(oa, ob, atol=1e-12, rtol=0) and np.allclose(la, lb, atol=1e-12, rtol=0)
+    # without the rotation the shift changes nothing either, with it off the
+    # window alone decides; with a different key set the outputs differ
+    on, ln = ref.attention_of(a, window_left=w)
+    assert not np.allclose(on, oa, atol=1e-6)
