@@ -218,7 +218,7 @@ def prefill_slice(b):
 
 
 def time_batch_call(b, steps, warmup, workers_decode=0, workers_prefill=0, pool_copies=2,
-                    window_left=-1):
+                    window_left=-1, rope_theta=0.0):
     """Plan once, then time the run call (decode/prefill kernels + merges) with
     HIP events on its stream.  Returns (mean ms, plan)."""
     import torch
@@ -240,7 +240,7 @@ def time_batch_call(b, steps, warmup, workers_decode=0, workers_prefill=0, pool_
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
     ws = torch.empty(plan.float_ws_bytes // 4 + 64, dtype=torch.float32, device=dev)
     params = fi.make_params(b.dtype, b.dtype, b.num_qo_heads, Hk, b.head_dim, b.page_size,
-                            b.sm_scale, b.soft_cap)
+                            b.sm_scale, b.soft_cap, rope_theta=rope_theta)
     qo_d, kvp_d, kvi_d, last_d = (None if b.qo_indptr is None else i32(b.qo_indptr),
                                   i32(b.kv_indptr), i32(b.kv_indices), i32(b.kv_last_page_len))
 
@@ -292,6 +292,7 @@ def secondary_measurements(args):
         "roofline_frac": round(max(nb / (HBM_PEAK_GBS * 1e9), fl / (BF16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3), 4)}
     out["append"] = time_append(b, args.side_steps)
     out["window"] = window_measurements(ps, args.side_steps)
+    out["rope"] = rope_measurements(ps, args.side_steps)
     del b, ps
     cb = wl.shared_prefix_cascade()
     ms_flat, _ = time_batch_call(cb.flat, args.side_steps, 3)
@@ -323,6 +324,31 @@ def window_measurements(ps, steps):
     out["prefill_slice"] = {"workload": "mixed_ragged_step prefill requests, window 1023",
                             "ms": round(ms, 4), "flops": fl,
                             "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                            "frac": round(fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    return out
+
+
+ROPE_THETA = 500000.0  # rotary base of the Llama-3 family
+
+
+def rope_measurements(ps, steps):
+    """Fused rotary embedding on q and k: the decode workload (two worker
+    counts: the rotary decode kernel runs two waves per SIMD) and the prefill
+    slice of the mixed step.  Same algorithmic bytes and flops as without it."""
+    import workloads as wl
+    import paged_kv_block_bsr_amd as fi
+    db = wl.llama8b_decode()
+    nb = decode_bytes(db)
+    out = {"rope_theta": ROPE_THETA, "decode": {"workload": "llama8b_decode, rotary embedding"}}
+    for w in (fi.fi_default_workers(fi.FI_KIND_DECODE, NUM_CUS, db.num_kv_heads), 2 * NUM_CUS // db.num_kv_heads):
+        ms, _ = time_batch_call(db, steps, 3, workers_decode=w, rope_theta=ROPE_THETA)
+        out["decode"][f"workers_{w}"] = {"us": round(ms * 1e3, 2), "gbs": round(nb / (ms * 1e-3) / 1e9, 1),
+                                         "frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del db
+    ms, _ = time_batch_call(ps, steps, 3, rope_theta=ROPE_THETA)
+    fl = prefill_flops(ps)
+    out["prefill_slice"] = {"workload": "mixed_ragged_step prefill requests, rotary embedding",
+                            "ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
                             "frac": round(fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
     return out
 

@@ -152,6 +152,20 @@ int fi_plan_bounds(int32_t batch_size, int64_t total_qo, int32_t num_qo_heads,
  *              (serving-engine page, "How FlashInfer Works": load balancing
  *              that survives CUDA graphs).  0: kernels without work are not
  *              launched.
+ *   rope_theta > 0: fused rotary embedding of q and k inside the kernels
+ *              (paper page: fused rotary embeddings among the attention
+ *              variants of its opening paragraph; "Customizable attention":
+ *              a query / key transform).  Rotate-half form: for d < D/2 the
+ *              pair (x[d], x[d + D/2]) turns by pos / rope_scale *
+ *              rope_theta^(-2d/D); key j of a request sits at position j,
+ *              query t at kv_len - qo_len + t.  The cache holds keys before
+ *              rotation; v is not rotated.  With bf16 storage the rotated
+ *              q and k are rounded to fp16 (round to nearest even,
+ *              components saturating at +-65504) for the QK^T product;
+ *              fp32 stays fp32.  <= 0: off.
+ *   rope_scale position divisor of the rotary embedding; <= 0 means 1.
+ *              The cascade call takes no rotary embedding (its levels do not
+ *              carry the keys' positions): FI_ERR_UNSUPPORTED.
  */
 typedef struct fi_attn_params {
   fi_dtype dtype;
@@ -163,6 +177,8 @@ typedef struct fi_attn_params {
   float sm_scale;
   float logits_soft_cap;
   int32_t graph_safe;
+  float rope_theta;
+  float rope_scale;
 } fi_attn_params;
 
 /*

@@ -85,7 +85,9 @@ class fi_attn_params(ctypes.Structure):
                 ("page_size", ctypes.c_int32),
                 ("sm_scale", ctypes.c_float),
                 ("logits_soft_cap", ctypes.c_float),
-                ("graph_safe", ctypes.c_int32)]
+                ("graph_safe", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float),
+                ("rope_scale", ctypes.c_float)]
 
 
 _lib = None
@@ -234,12 +236,15 @@ def fi_plan_bounds(batch_size, total_qo, num_qo_heads, num_kv_heads, head_dim, w
 
 
 def make_params(q_dtype, out_dtype, num_qo_heads, num_kv_heads, head_dim, page_size, sm_scale=0.0,
-                logits_soft_cap=0.0, graph_safe=False) -> fi_attn_params:
+                logits_soft_cap=0.0, graph_safe=False, rope_theta=0.0, rope_scale=1.0) -> fi_attn_params:
     """``graph_safe``: launch every kernel of a call whatever the plan, so a
-    call captured into a graph stays valid for later plans of the same shapes."""
+    call captured into a graph stays valid for later plans of the same shapes.
+    ``rope_theta`` > 0: fused rotary embedding of q and k (``rope_scale``
+    divides the positions)."""
     return fi_attn_params(_dtype_code(q_dtype), _dtype_code(out_dtype), num_qo_heads,
                           num_kv_heads, head_dim, page_size, float(sm_scale),
-                          float(logits_soft_cap), int(bool(graph_safe)))
+                          float(logits_soft_cap), int(bool(graph_safe)), float(rope_theta),
+                          float(rope_scale))
 
 
 def fi_batch_decode_paged(plan: Plan, plan_dev, params: fi_attn_params, q, kv_pool,

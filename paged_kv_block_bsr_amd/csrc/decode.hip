@@ -54,6 +54,7 @@ struct DecodeParams {
   float cap;           // soft-cap; 0 = off
   float inv_cap;       // 1 / cap (0 when off)
   int32_t window;      // sliding window: keys seen before the query's own; -1 = none
+  uint32_t rope_f[kRopeMaxPairs];  // rotary turn per position of pair d (2^-32 revolutions)
 };
 
 template <typename T, int D>
@@ -68,12 +69,17 @@ struct Shape {
 
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 
-template <typename T, int NK>
+// S = K Q^T for one chunk.  F16: the operands are fp16 (rotated q and k)
+// rather than the storage type.
+template <typename T, int NK, bool F16 = false>
 __device__ __forceinline__ f32x4_t qk_mfma(const u32x4_t (&kp)[NK], const u32x4_t (&qp)[NK]) {
   f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int p = 0; p < NK; ++p) {
-    if constexpr (T::kBytes == 2) {
+    if constexpr (T::kBytes == 2 && F16) {
+      s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, kp[p]),
+                                                 __builtin_bit_cast(f16x8_t, qp[p]), s, 0, 0, 0);
+    } else if constexpr (T::kBytes == 2) {
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kp[p]),
                                                   __builtin_bit_cast(bf16x8_t, qp[p]), s, 0, 0, 0);
     } else {
@@ -94,11 +100,17 @@ __device__ __forceinline__ void store_out(uint8_t* base, int64_t idx, float v) {
     reinterpret_cast<float*>(base)[idx] = v;
 }
 
-template <typename T, int D, int G, bool FAST, typename OT>
+template <typename T, int D, int G, bool FAST, typename OT, bool ROPE>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams a) {
   using SH = Shape<T, D>;
   constexpr int E = SH::E, NC = SH::NC, NL = SH::NL, NK = SH::NK;
   constexpr int TB = T::kBytes;
+  // rotary table in LDS (the lanes read it with their own dims)
+  __shared__ uint32_t rope_tab[ROPE ? D / 2 : 1];
+  if constexpr (ROPE) {
+    for (int i = threadIdx.x; i < D / 2; i += kThreads) rope_tab[i] = a.rope_f[i];
+    __syncthreads();
+  }
 
   __shared__ __align__(16) float p_lds[kWaves][G][kChunk];
   __shared__ float alpha_lds[kWaves][G];
@@ -155,6 +167,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams a) {
       for (int p = 0; p < NK; ++p) {
         qp[p] = load16(qb + (int64_t)(4 * p + kq) * 16);
         if (hS >= G) qp[p] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+      // rotary embedding: the query sits at position kv_len - 1; piece
+      // 4 p + kq holds dims E (4 p + kq) .., its partner D / 2 further
+      if constexpr (ROPE) {
+#pragma unroll
+        for (int p = 0; p < NK / 2; ++p)
+          rope_pieces<T>(qp[p], qp[p + NK / 2], (const FI_LDS uint32_t*)rope_tab + E * (4 * p + kq), kv_len - 1);
       }
     }
 
@@ -213,7 +232,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams a) {
 
     auto compute_chunk = [&](int c, const u32x4_t (&kb)[NK], const u32x4_t (&vb)[NL]) {
       const int cs = t0 + c * kChunk;
-      f32x4_t s = qk_mfma<T, NK>(kb, qp);
+      f32x4_t s;
+      if constexpr (ROPE) {  // the lane's key (token cs + tk) turned to its position
+        u32x4_t kr[NK];
+#pragma unroll
+        for (int p = 0; p < NK; ++p) kr[p] = kb[p];
+#pragma unroll
+        for (int p = 0; p < NK / 2; ++p)
+          rope_pieces<T>(kr[p], kr[p + NK / 2], (const FI_LDS uint32_t*)rope_tab + E * (4 * p + kq), cs + tk);
+        s = qk_mfma<T, NK, true>(kr, qp);
+      } else {
+        s = qk_mfma<T, NK>(kb, qp);
+      }
       float x[4];
       if (a.cap > 0.f) {
         const float c_in = a.scale * a.inv_cap, c_out = a.cap * kLog2e;
@@ -378,14 +408,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams a) {
 // vmcnt itself before reading a stage.
 // ---------------------------------------------------------------------------
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
-#define FI_LDS __attribute__((address_space(3)))
 
 // s_waitcnt with vmcnt <= n and no wait on the other counters (gfx9 encoding)
 #define FI_WAIT_VMCNT(n) \
   __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
-template <int D, int G, typename OT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+// 3 waves per SIMD; the rotary variant at D = 128 needs the registers of 2
+template <int D, int G, typename OT, bool ROPE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ROPE && D == 128 ? 2 : 3, ROPE && D == 128 ? 2 : 3)))
 void decode_mfma_kernel(DecodeParams a) {
   constexpr int RB = D * 2;              // bytes of one K / V row of one head
   constexpr int NP = RB / 16;            // 16-byte pieces per row
@@ -398,6 +428,12 @@ void decode_mfma_kernel(DecodeParams a) {
   __shared__ __align__(16) uint8_t vring[kWaves][2][kStage];
   __shared__ float m_lds[kWaves][G];
   __shared__ float l_lds[kWaves][G];
+  // rotary table in LDS (the lanes read it with their own dims)
+  __shared__ uint32_t rope_tab[ROPE ? D / 2 : 1];
+  if constexpr (ROPE) {
+    for (int i = threadIdx.x; i < D / 2; i += kThreads) rope_tab[i] = a.rope_f[i];
+    __syncthreads();
+  }
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -522,6 +558,12 @@ void decode_mfma_kernel(DecodeParams a) {
         qp[p] = load16(qb + (4 * p + kq) * 16);
         if (hS >= G) qp[p] = u32x4_t{0u, 0u, 0u, 0u};
       }
+      if constexpr (ROPE) {  // the query sits at position kv_len - 1
+#pragma unroll
+        for (int p = 0; p < NK / 2; ++p)
+          rope_pieces<BF16>(qp[p], qp[p + NK / 2], (const FI_LDS uint32_t*)rope_tab + 8 * (4 * p + kq),
+                            cur.kv_len - 1);
+      }
     }
     float m_run = neg_inf();
     float l_part = 0.f;
@@ -536,7 +578,18 @@ void decode_mfma_kernel(DecodeParams a) {
 
     auto compute = [&](int c, int st, const u32x4_t (&kb)[NK]) {
       const int cs = t0 + c * kChunk;
-      f32x4_t s = qk_mfma<BF16, NK>(kb, qp);
+      f32x4_t s;
+      if constexpr (ROPE) {  // the lane's key (token cs + tk) turned to its position
+        u32x4_t kr[NK];
+#pragma unroll
+        for (int p = 0; p < NK; ++p) kr[p] = kb[p];
+#pragma unroll
+        for (int p = 0; p < NK / 2; ++p)
+          rope_pieces<BF16>(kr[p], kr[p + NK / 2], (const FI_LDS uint32_t*)rope_tab + 8 * (4 * p + kq), cs + tk);
+        s = qk_mfma<BF16, NK, true>(kr, qp);
+      } else {
+        s = qk_mfma<BF16, NK>(kb, qp);
+      }
       float x[4];
       if (a.cap > 0.f) {
         const float c_in = a.scale * a.inv_cap, c_out = a.cap * kLog2e;
@@ -666,40 +719,45 @@ void decode_mfma_kernel(DecodeParams a) {
   }
 }
 
-template <int D, int G, typename OT>
+template <int D, int G, typename OT, bool ROPE>
 int launch_mfma(const RunArgs& r, const DecodeParams& p) {
   dim3 grid(r.workers, r.Hk), block(kThreads);
-  hipLaunchKernelGGL((decode_mfma_kernel<D, G, OT>), grid, block, 0, (hipStream_t)r.hip_stream, p);
+  hipLaunchKernelGGL((decode_mfma_kernel<D, G, OT, ROPE>), grid, block, 0, (hipStream_t)r.hip_stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(FI_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return FI_OK;
 }
 
-template <typename T, int D, int G, bool FAST, typename OT>
+template <typename T, int D, int G, bool FAST, typename OT, bool ROPE>
 int launch_t(const RunArgs& r, const DecodeParams& p) {
   dim3 grid(r.workers, r.Hk), block(kThreads);
-  hipLaunchKernelGGL((decode_kernel<T, D, G, FAST, OT>), grid, block, 0,
+  hipLaunchKernelGGL((decode_kernel<T, D, G, FAST, OT, ROPE>), grid, block, 0,
                      (hipStream_t)r.hip_stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(FI_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return FI_OK;
 }
 
-template <typename T, int D, int G, typename OT>
+template <typename T, int D, int G, typename OT, bool ROPE>
 int launch_fast(const RunArgs& r, const DecodeParams& p) {
   if constexpr (T::kBytes == 2) {
-    if (p.page_shift >= 0) return launch_mfma<D, G, OT>(r, p);
+    if (p.page_shift >= 0) return launch_mfma<D, G, OT, ROPE>(r, p);
   }
-  return p.page_shift >= 0 ? launch_t<T, D, G, true, OT>(r, p) : launch_t<T, D, G, false, OT>(r, p);
+  return p.page_shift >= 0 ? launch_t<T, D, G, true, OT, ROPE>(r, p) : launch_t<T, D, G, false, OT, ROPE>(r, p);
+}
+
+template <typename T, int D, int G, typename OT>
+int launch_rope(const RunArgs& r, const DecodeParams& p) {
+  return r.rope ? launch_fast<T, D, G, OT, true>(r, p) : launch_fast<T, D, G, OT, false>(r, p);
 }
 
 template <typename T, int D, typename OT>
 int launch_g(const RunArgs& r, const DecodeParams& p) {
   switch (r.G) {
-    case 1: return launch_fast<T, D, 1, OT>(r, p);
-    case 2: return launch_fast<T, D, 2, OT>(r, p);
-    case 4: return launch_fast<T, D, 4, OT>(r, p);
-    case 8: return launch_fast<T, D, 8, OT>(r, p);
+    case 1: return launch_rope<T, D, 1, OT>(r, p);
+    case 2: return launch_rope<T, D, 2, OT>(r, p);
+    case 4: return launch_rope<T, D, 4, OT>(r, p);
+    case 8: return launch_rope<T, D, 8, OT>(r, p);
   }
   return set_error(FI_ERR_UNSUPPORTED, "decode: group size %d", r.G);
 }
@@ -741,6 +799,7 @@ int launch_decode(const RunArgs& r) {
   p.cap = r.soft_cap;
   p.inv_cap = r.soft_cap > 0.f ? 1.f / r.soft_cap : 0.f;
   p.window = r.window;
+  for (int i = 0; i < kRopeMaxPairs; ++i) p.rope_f[i] = r.rope_f[i];
   if (r.dtype == FI_BF16 && r.out_dtype == FI_BF16) return launch_d<BF16, BF16>(r, p);
   if (r.dtype == FI_BF16 && r.out_dtype == FI_F32) return launch_d<BF16, F32>(r, p);
   if (r.dtype == FI_F32 && r.out_dtype == FI_F32) return launch_d<F32, F32>(r, p);

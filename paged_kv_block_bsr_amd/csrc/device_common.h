@@ -11,6 +11,8 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -72,6 +74,64 @@ __device__ __forceinline__ float piece_elem<F32>(const u32x4_t& v, int i) {
 
 __device__ __forceinline__ u32x4_t load16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+#define FI_LDS __attribute__((address_space(3)))
+
+// ---- rotary embedding (rotate-half form: the pair (x[d], x[d + D/2]) turns
+// by pos / scale * theta^(-2d/D)).  The host supplies, per pair d, the turn
+// per position as a 32-bit fixed-point fraction of a revolution; the angle of
+// a position is that times pos modulo 2^32 (exact integer arithmetic, whole
+// turns drop out), and v_sin / v_cos take it in revolutions.  Tables are read
+// from LDS through address-space-3 pointers only: a flat load would also count
+// in the vector-memory counter the kernels wait on by hand.
+constexpr int kRopeMaxPairs = 64;
+
+__device__ __forceinline__ void rope_cos_sin(uint32_t f, int pos, float& c, float& s) {
+  const float rev = (float)(int32_t)((uint32_t)pos * f) * 0x1p-32f;  // in [-0.5, 0.5)
+  c = __builtin_amdgcn_cosf(rev);
+  s = __builtin_amdgcn_sinf(rev);
+}
+
+// Two fp32 values as an fp16 pair (lo in bits 0..15), round to nearest even,
+// saturating at +-65504 instead of overflowing.
+__device__ __forceinline__ uint32_t pack_f16x2_sat(float lo, float hi) {
+  lo = __builtin_amdgcn_fmed3f(lo, -65504.f, 65504.f);
+  hi = __builtin_amdgcn_fmed3f(hi, -65504.f, 65504.f);
+  const f16x2_t v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Rotate the pairs held by two 16-byte pieces of storage type T: `lo` has
+// dims d0 .. d0 + n - 1, `hi` the same dims + D/2 (n = 16 / sizeof(T)); f is
+// the table at d0.  bf16 pieces come back as fp16 (11-bit significand, round
+// to nearest even, saturating): the rotated values feed fp16 matrix-core
+// products, whose rounding keeps the logits within the attention tolerance
+// where bf16's 8 bits would not.  fp32 pieces stay fp32.
+template <typename T>
+__device__ __forceinline__ void rope_pieces(u32x4_t& lo, u32x4_t& hi, const FI_LDS uint32_t* f,
+                                            int pos) {
+  if constexpr (T::kBytes == 2) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float c0, s0, c1, s1;
+      rope_cos_sin(f[2 * w], pos, c0, s0);
+      rope_cos_sin(f[2 * w + 1], pos, c1, s1);
+      const float a0 = bf16_lo(lo[w]), a1 = bf16_hi(lo[w]);
+      const float b0 = bf16_lo(hi[w]), b1 = bf16_hi(hi[w]);
+      lo[w] = pack_f16x2_sat(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
+      hi[w] = pack_f16x2_sat(b0 * c0 + a0 * s0, b1 * c1 + a1 * s1);
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float c, s;
+      rope_cos_sin(f[w], pos, c, s);
+      const float a = __uint_as_float(lo[w]), b = __uint_as_float(hi[w]);
+      lo[w] = __float_as_uint(a * c - b * s);
+      hi[w] = __float_as_uint(b * c + a * s);
+    }
+  }
 }
 
 }  // namespace fi

@@ -44,6 +44,8 @@ int check_params(const fi_attn_params* p) {
   if (p->page_size < 1) return set_error(FI_ERR_INVALID_ARG, "page_size");
   if (!std::isfinite(p->sm_scale) || !std::isfinite(p->logits_soft_cap) || p->logits_soft_cap < 0)
     return set_error(FI_ERR_INVALID_ARG, "sm_scale / logits_soft_cap");
+  if (!std::isfinite(p->rope_theta) || !std::isfinite(p->rope_scale))
+    return set_error(FI_ERR_INVALID_ARG, "rope_theta / rope_scale");
   return FI_OK;
 }
 
@@ -63,6 +65,22 @@ int check_plan(const int32_t* ph, const fi_attn_params* p, const char* who) {
       return set_error(FI_ERR_PLAN_MISMATCH, "%s: corrupted stream descriptor", who);
   }
   return FI_OK;
+}
+
+// Rotary table: for pair d < D/2 the turn per position, theta^(-2d/D) /
+// scale radians, as a fraction of a revolution in 2^-32 units (whole turns
+// dropped).  The kernels multiply it by the position modulo 2^32.
+void rope_table(const fi_attn_params* p, RunArgs& a) {
+  a.rope = p->rope_theta > 0.f;
+  for (int d = 0; d < 64; ++d) a.rope_f[d] = 0;
+  if (!a.rope) return;
+  const double scale = p->rope_scale > 0.f ? (double)p->rope_scale : 1.0;
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int d = 0; d < p->head_dim / 2; ++d) {
+    const double rev = std::pow((double)p->rope_theta, -2.0 * d / p->head_dim) / scale / two_pi;
+    const double frac = rev - std::floor(rev);
+    a.rope_f[d] = (uint32_t)(uint64_t)std::llround(std::ldexp(frac, 32));  // 2^32 wraps to 0
+  }
 }
 
 float resolve_scale(const fi_attn_params* p) {
@@ -93,6 +111,7 @@ RunArgs base_args(const int32_t* plan_dev, const fi_attn_params* p, const void* 
   a.G = a.Hq / a.Hk;
   a.causal = ph[H_CAUSAL];
   a.window = ph[H_WINDOW];
+  rope_table(p, a);
   a.sm_scale = resolve_scale(p);
   a.soft_cap = p->logits_soft_cap;
   a.dtype = p->dtype;
@@ -245,6 +264,8 @@ int fi_cascade(const int32_t* plan0_host, const int32_t* plan0_dev, const int32_
   if ((rc = check_plan(plan1_host, params, "fi_cascade level 1"))) return rc;
   if (plan0_host[H_CAUSAL] != 0)
     return set_error(FI_ERR_PLAN_MISMATCH, "fi_cascade: level-0 plan must be non-causal");
+  if (params->rope_theta > 0.f)
+    return set_error(FI_ERR_UNSUPPORTED, "fi_cascade: the rotary embedding is not supported");
   if (plan0_host[H_WINDOW] >= 0 || plan1_host[H_WINDOW] >= 0)
     return set_error(FI_ERR_UNSUPPORTED, "fi_cascade: plans with a sliding window are not supported");
   if (plan0_host[H_TOTAL_QO] != plan1_host[H_TOTAL_QO])

@@ -34,6 +34,8 @@ struct RunArgs {
   int32_t Hq, Hk, D, P, G;
   int32_t causal;
   int32_t window;               // sliding window (keys before the query's own); -1 = none
+  int32_t rope;                 // rotary embedding on q and k (rope_f holds its table)
+  uint32_t rope_f[64];          // per pair d < D/2: turn per position, 2^-32 revolutions
   float sm_scale;
   float soft_cap;
   fi_dtype dtype, out_dtype;

@@ -1,6 +1,6 @@
 // prefill.hip -- launches of the batch-prefill kernel (prefill_kernel.h):
-// the kernels without a sliding window are built here, the windowed ones in
-// prefill_window.hip.
+// the kernels without a sliding window or rotary embedding are built here,
+// the windowed ones in prefill_window.hip, the rotary ones in prefill_rope.hip.
 #include "prefill_kernel.h"
 
 namespace fi {
@@ -39,8 +39,10 @@ int launch_prefill(const RunArgs& r) {
     while ((1 << sh) < r.P) ++sh;
     p.page_shift = sh;
   }
+  for (int i = 0; i < kRopeMaxPairs; ++i) p.rope_f[i] = r.rope_f[i];
+  if (r.rope) return launch_prefill_rope(r, p);
   if (r.window >= 0) return launch_prefill_window(r, p);
-  return launch_mode<false>(r, p);
+  return launch_mode<false, false>(r, p);
 }
 
 }  // namespace fi

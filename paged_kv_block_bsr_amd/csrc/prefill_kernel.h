@@ -1,7 +1,8 @@
 // prefill_kernel.h -- persistent ragged batch-prefill kernel over a paged KV cache
 // (gfx950, bf16, MFMA), included by prefill.hip (kernels without a sliding
-// window) and prefill_window.hip (with one): two translation units that
-// build in parallel.
+// window or rotary embedding), prefill_window.hip (with a window) and
+// prefill_rope.hip (with the rotary embedding, window or not): translation
+// units that build in parallel.
 //
 // Operation (FlashInfer pages): every query token of a request attends to the
 // request's KV tokens, gathered page by page through kv_indices
@@ -66,6 +67,7 @@ struct PrefillParams {
   float cap;
   float inv_cap;
   int32_t window;      // sliding window: keys seen before the query's own (kernels built with WIN)
+  uint32_t rope_f[kRopeMaxPairs];  // rotary turn per position of pair d (kernels built with ROPE)
 };
 
 namespace {
@@ -78,8 +80,6 @@ constexpr int kVStride = kTileK + 8;  // V^T row stride (elements): 144 B, confl
 constexpr float kMaxSlack = 8.f;      // log2-domain headroom of the lazily updated running max
 
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
-typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
-typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
 
 // s_waitcnt with vmcnt <= n and no wait on the other counters (gfx9 encoding)
 #define FI_WAIT_VMCNT(n) \
@@ -121,7 +121,6 @@ __device__ __forceinline__ float half_sum(float x) {
 // feeds to one 16-key k-step of the PV product are contiguous.
 __device__ __forceinline__ int vt_pos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
-#define FI_LDS __attribute__((address_space(3)))
 
 template <int D>
 struct PShape {
@@ -135,7 +134,7 @@ struct PShape {
   static constexpr int VThreads = 16 * VPiecesRow;             // threads staging V: 4 keys x 1 piece each
 };
 
-template <int D, int G, bool FAST, bool CAP, bool WIN, typename OT>
+template <int D, int G, bool FAST, bool CAP, bool WIN, bool ROPE, typename OT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillParams a) {
   using SH = PShape<D>;
@@ -147,6 +146,11 @@ void prefill_kernel(PrefillParams a) {
   __shared__ __align__(16) uint8_t k_lds1[kTileK * SH::KRow];
   __shared__ __align__(16) uint16_t v_lds0[D * kVStride];
   __shared__ __align__(16) uint16_t v_lds1[D * kVStride];
+  __shared__ uint32_t rope_tab[ROPE ? D / 2 : 1];  // rotary table, read with the lanes' own dims
+  if constexpr (ROPE) {
+    for (int i = threadIdx.x; i < D / 2; i += kThreads) rope_tab[i] = a.rope_f[i];
+    __syncthreads();
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -357,6 +361,37 @@ void prefill_kernel(PrefillParams a) {
       qp[ks] = __builtin_bit_cast(bf16x8_t, load16(qb + (16 * ks + 8 * hh) * 2));
   };
 
+  // ---- rotary embedding.  Queries are turned in registers once per item
+  // (lane dims 16 ks + 8 hh .. + 8; the partner of ks is ks + KSteps / 2).
+  // Keys are turned once per workgroup, in LDS, after a tile has landed and
+  // before it is read: thread t takes key t / 4 and D / 64 piece pairs
+  // (c, c + D / 16) of its row, in place.  Both come out as fp16, and the
+  // QK^T product of these kernels runs on the fp16 matrix-core instruction.
+  auto rope_q = [&](int pos) {
+#pragma unroll
+    for (int ks = 0; ks < SH::KSteps / 2; ++ks) {
+      u32x4_t lo = __builtin_bit_cast(u32x4_t, qp[ks]), hi = __builtin_bit_cast(u32x4_t, qp[ks + SH::KSteps / 2]);
+      rope_pieces<BF16>(lo, hi, (const FI_LDS uint32_t*)rope_tab + 16 * ks + 8 * hh, pos);
+      qp[ks] = __builtin_bit_cast(bf16x8_t, lo);
+      qp[ks + SH::KSteps / 2] = __builtin_bit_cast(bf16x8_t, hi);
+    }
+  };
+  auto rope_k = [&](uint8_t* kb, int ts) {
+    constexpr int PPT = D / 64, HALF = D / 16;
+    const int key = tid >> 2;
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const int c = (tid & 3) * PPT + j;
+      uint8_t* row = kb + key * SH::KRow;
+      u32x4_t* plo = reinterpret_cast<u32x4_t*>(row + ((c ^ (key & (SH::KPiecesRow - 1))) * 16));
+      u32x4_t* phi = reinterpret_cast<u32x4_t*>(row + (((c + HALF) ^ (key & (SH::KPiecesRow - 1))) * 16));
+      u32x4_t lo = *plo, hi = *phi;
+      rope_pieces<BF16>(lo, hi, (const FI_LDS uint32_t*)rope_tab + 8 * c, ts + key);
+      *plo = lo;
+      *phi = hi;
+    }
+  };
+
   // the worker's first item: query rows, tile 0 and the page ids of tile 1
   Item item = uniform(load_item(it_begin));
   KPages pk{};
@@ -429,8 +464,13 @@ void prefill_kernel(PrefillParams a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[e] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < SH::KSteps; ++ks)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kop[ks]), qp[ks], s, 0, 0, 0);
+      for (int ks = 0; ks < SH::KSteps; ++ks) {
+        if constexpr (ROPE)  // rotated q and k are fp16
+          s = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, kop[ks]),
+                                                     __builtin_bit_cast(f16x8_t, qp[ks]), s, 0, 0, 0);
+        else
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kop[ks]), qp[ks], s, 0, 0, 0);
+      }
     };
     // V^T operands of block b: dims 32 d + l32, k-steps k of 16 keys
     auto vread = [&](const uint16_t* vb, int b, u32x4_t (&vop)[2][SH::DBlocks]) {
@@ -534,6 +574,13 @@ void prefill_kernel(PrefillParams a) {
     if (ntiles > 0) store_v(v_lds0);
     FI_WAIT_VMCNT(0);
     __syncthreads();
+    if constexpr (ROPE) {  // the query rows and key tile 0 have landed: turn them
+      rope_q(causal_off + tok);
+      if (ntiles > 0) {
+        rope_k(k_lds0, t0);
+        __syncthreads();
+      }
+    }
     // the next item's record has landed: the page ids of its first tile
     // (with pages of any size, 8 ids a lane: fetched after the loop instead,
     // as holding them through it would spill)
@@ -583,6 +630,12 @@ void prefill_kernel(PrefillParams a) {
       store_v(vb_next);
       FI_WAIT_VMCNT(0);
       __syncthreads();
+      if constexpr (ROPE) {  // key tile n + 1 has landed in kb_next: turn it before it is read
+        if (n + 1 < ntiles) {
+          rope_k(kb_next, t0 + (n + 1) * kTileK);
+          __syncthreads();
+        }
+      }
     };
     auto step_any = [&](int n, auto cur) {
       const int ts = t0 + n * kTileK;
@@ -653,50 +706,51 @@ void prefill_kernel(PrefillParams a) {
   }
 }
 
-template <int D, int G, bool FAST, bool CAP, bool WIN, typename OT>
+template <int D, int G, bool FAST, bool CAP, bool WIN, bool ROPE, typename OT>
 int launch_k(const RunArgs& r, const PrefillParams& p) {
   dim3 grid(r.workers * r.Hk), block(kThreads);
-  hipLaunchKernelGGL((prefill_kernel<D, G, FAST, CAP, WIN, OT>), grid, block, 0, (hipStream_t)r.hip_stream, p);
+  hipLaunchKernelGGL((prefill_kernel<D, G, FAST, CAP, WIN, ROPE, OT>), grid, block, 0, (hipStream_t)r.hip_stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(FI_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
   return FI_OK;
 }
 
-template <int D, int G, bool WIN, typename OT>
+template <int D, int G, bool WIN, bool ROPE, typename OT>
 int launch_t(const RunArgs& r, const PrefillParams& p) {
   const bool fast = p.page_shift >= 0, cap = p.cap > 0.f;
-  if (fast) return cap ? launch_k<D, G, true, true, WIN, OT>(r, p) : launch_k<D, G, true, false, WIN, OT>(r, p);
-  return cap ? launch_k<D, G, false, true, WIN, OT>(r, p) : launch_k<D, G, false, false, WIN, OT>(r, p);
+  if (fast) return cap ? launch_k<D, G, true, true, WIN, ROPE, OT>(r, p) : launch_k<D, G, true, false, WIN, ROPE, OT>(r, p);
+  return cap ? launch_k<D, G, false, true, WIN, ROPE, OT>(r, p) : launch_k<D, G, false, false, WIN, ROPE, OT>(r, p);
 }
 
-template <int D, bool WIN, typename OT>
+template <int D, bool WIN, bool ROPE, typename OT>
 int launch_g(const RunArgs& r, const PrefillParams& p) {
   switch (r.G) {
-    case 1: return launch_t<D, 1, WIN, OT>(r, p);
-    case 2: return launch_t<D, 2, WIN, OT>(r, p);
-    case 4: return launch_t<D, 4, WIN, OT>(r, p);
-    case 8: return launch_t<D, 8, WIN, OT>(r, p);
+    case 1: return launch_t<D, 1, WIN, ROPE, OT>(r, p);
+    case 2: return launch_t<D, 2, WIN, ROPE, OT>(r, p);
+    case 4: return launch_t<D, 4, WIN, ROPE, OT>(r, p);
+    case 8: return launch_t<D, 8, WIN, ROPE, OT>(r, p);
   }
   return set_error(FI_ERR_UNSUPPORTED, "prefill: group size %d", r.G);
 }
 
-template <bool WIN, typename OT>
+template <bool WIN, bool ROPE, typename OT>
 int launch_d(const RunArgs& r, const PrefillParams& p) {
-  if (r.D == 64) return launch_g<64, WIN, OT>(r, p);
-  if (r.D == 128) return launch_g<128, WIN, OT>(r, p);
+  if (r.D == 64) return launch_g<64, WIN, ROPE, OT>(r, p);
+  if (r.D == 128) return launch_g<128, WIN, ROPE, OT>(r, p);
   return set_error(FI_ERR_UNSUPPORTED, "prefill: head_dim %d", r.D);
 }
 
-// The kernels of one window mode, for the output type of the call.
-template <bool WIN>
+// The kernels of one window / rotary mode, for the output type of the call.
+template <bool WIN, bool ROPE>
 int launch_mode(const RunArgs& r, const PrefillParams& p) {
-  if (r.out_dtype == FI_BF16) return launch_d<WIN, BF16>(r, p);
-  return launch_d<WIN, F32>(r, p);
+  if (r.out_dtype == FI_BF16) return launch_d<WIN, ROPE, BF16>(r, p);
+  return launch_d<WIN, ROPE, F32>(r, p);
 }
 
 }  // namespace
 
-// defined in prefill_window.hip
+// defined in prefill_window.hip and prefill_rope.hip
 int launch_prefill_window(const RunArgs& r, const PrefillParams& p);
+int launch_prefill_rope(const RunArgs& r, const PrefillParams& p);
 
 }  // namespace fi

@@ -5,6 +5,6 @@
 
 namespace fi {
 
-int launch_prefill_window(const RunArgs& r, const PrefillParams& p) { return launch_mode<true>(r, p); }
+int launch_prefill_window(const RunArgs& r, const PrefillParams& p) { return launch_mode<true, false>(r, p); }
 
 }  // namespace fi

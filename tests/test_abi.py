@@ -197,6 +197,25 @@ def test_cascade_rejects_windowed_plans_without_a_gpu():
     assert rc == fi.binding.FI_ERR_UNSUPPORTED and "window" in fi.fi_last_error()
 
 
+def test_rope_arguments_are_checked_without_a_gpu():
+    torch = __import__("torch")
+    plan = fi.fi_plan(None, [0, 2], [3], page_size=16, num_qo_heads=8, num_kv_heads=2,
+                      head_dim=128, causal=True, workers_decode=2)
+    L = fi.lib()
+    params = fi.make_params(torch.bfloat16, torch.bfloat16, 8, 2, 128, 16, rope_theta=float("inf"))
+    rc = L.fi_batch_decode_paged(plan.host_ptr(), 16, ctypes.byref(params), 16, 16, 10, 16, 16, 16,
+                                 16, None, 16, 1 << 20, None)
+    assert rc == fi.binding.FI_ERR_INVALID_ARG and "rope" in fi.fi_last_error()
+    kw = dict(page_size=16, num_qo_heads=8, num_kv_heads=2, head_dim=128, workers_decode=2,
+              workers_prefill=2)
+    p0 = fi.fi_plan([0, 1], [0, 2], [3], causal=False, **kw)
+    p1 = fi.fi_plan([0, 1], [0, 1], [5], causal=True, **kw)
+    params = fi.make_params(torch.bfloat16, torch.bfloat16, 8, 2, 128, 16, rope_theta=10000.0)
+    rc = L.fi_cascade(p0.host_ptr(), 16, 16, 16, 16, 16, p1.host_ptr(), 16, 16, 16, 16, 16,
+                      ctypes.byref(params), 16, 16, 10, 16, None, 16, 1 << 24, None)
+    assert rc == fi.binding.FI_ERR_UNSUPPORTED and "rotary" in fi.fi_last_error()
+
+
 def test_append_rejects_bad_arguments():
     L = fi.lib()
     args = lambda dtype=fi.FI_BF16, n=5, hk=8, d=128: (None, None, dtype, None, 1, n, None, 1, 16, hk, d,
