@@ -48,6 +48,7 @@ struct DecodeParams {
   int64_t pool_pages;
   int32_t Hq, Hk, P;
   int32_t page_shift;  // log2(P) when P is a power of two >= 16, else -1
+  int32_t small_shift; // log2(P) when P is 1, 2, 4 or 8, else -1
   int32_t stream_at;
   float scale_log2;    // sm_scale * log2(e)
   float scale;         // sm_scale
@@ -392,7 +393,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 decode with page_size a power of two >= 16: P.V on the matrix cores.
+// bf16 decode with page_size a power of two: P.V on the matrix cores.  Pages
+// of >= 16 tokens hold a whole chunk (one page id per chunk); with pages of
+// 1, 2, 4 or 8 tokens (SMALLP: the column-vector BSR of the serving-engine
+// page, "One format for every KV layout") a chunk spans several pages and
+// each lane looks up the page of its own token.
 //
 // Per wave and 16-token chunk: K goes global -> VGPRs as the A operand of
 // S = K Q^T (v_mfma_f32_16x16x32_bf16, as above); V goes global -> LDS by
@@ -414,7 +419,7 @@ typedef __attribute__((ext_vector_type(4))) short s16x4_t;
   __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
 // 3 waves per SIMD; the rotary variant at D = 128 needs the registers of 2
-template <int D, int G, typename OT, bool ROPE>
+template <int D, int G, typename OT, bool ROPE, bool SMALLP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ROPE && D == 128 ? 2 : 3, ROPE && D == 128 ? 2 : 3)))
 void decode_mfma_kernel(DecodeParams a) {
   constexpr int RB = D * 2;              // bytes of one K / V row of one head
@@ -424,6 +429,9 @@ void decode_mfma_kernel(DecodeParams a) {
   constexpr int NB = D / 16;             // 16-dim output blocks
   constexpr int kStage = kChunk * RB;    // bytes of one V stage
   static_assert(NK == NV, "one K and one V load per 32 dims");
+  // vector-memory operations issued per chunk: K and V loads, and with small
+  // pages the page-id load of the chunk two ahead
+  constexpr int kChunkOps = 2 * NK + (SMALLP ? 1 : 0);
 
   __shared__ __align__(16) uint8_t vring[kWaves][2][kStage];
   __shared__ float m_lds[kWaves][G];
@@ -495,9 +503,38 @@ void decode_mfma_kernel(DecodeParams a) {
     const int c = wave + kWaves * (64 * batch + lane);
     return c < x.nch ? a.kv_indices[x.kvb + ((x.t0 + c * kChunk) >> a.page_shift)] : 0;
   };
+  // SMALLP (pages of 1, 2, 4 or 8 tokens): a chunk spans several pages, so
+  // every lane looks up the page of its own token -- token tk of the wave's
+  // kth chunk, clamped to the item's last key like the loads below -- raw,
+  // two chunks ahead of its use.  The load is issued even for chunks past
+  // the item's end (it then reads the item's first page id), so that every
+  // chunk issues the same number of memory operations, which the waits in
+  // the chunk loop count on.  Needs x.nch >= 1.
+  auto load_id = [&](const Ctx& x, int kth) -> int {
+    const int c = wave + kWaves * kth;
+    const int tok = min(x.t0 + c * kChunk + tk, x.t1 - 1);
+    return a.kv_indices[x.kvb + (c < x.nch ? tok >> a.small_shift : 0)];
+  };
   // K -> registers, V -> LDS stage `st` for the wave's kth chunk c
   auto issue = [&](const Ctx& x, int pid_vec, int c, int kth, int st, u32x4_t (&kb)[NK]) {
     const int cs = x.t0 + c * kChunk;
+    if constexpr (SMALLP) {
+      // pid_vec is this lane's own page id (token tk).  K piece 4 p + kq and
+      // V piece 4 k + kq of that token: V load k of lane l lands at stage
+      // bytes k 1024 + 16 l, i.e. piece 4 k + l / 16 of token l % 16.
+      const int64_t page = (uint32_t)pid_vec < (uint64_t)a.pool_pages ? pid_vec : 0;  // never outside the pool
+      const int tok = cs + min(tk, x.t1 - 1 - cs);
+      const uint8_t* kaddr = a.kv + (page * page_stride + (int64_t)(tok & (P - 1)) * tok_stride + (int64_t)g * D) * 2;
+#pragma unroll
+      for (int p = 0; p < NK; ++p) kb[p] = load16(kaddr + (4 * p + kq) * 16);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < NV; ++k)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(kaddr + half_stride * 2 + (4 * k + kq) * 16),
+                                         (FI_LDS void*)(&vring[wave][st][k * 1024]), 16, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      return;
+    }
     const int pid = __builtin_amdgcn_readlane(pid_vec, kth & 63);
     const int64_t page = (uint32_t)pid < (uint64_t)a.pool_pages ? pid : 0;  // never read outside the pool
     const int slot0 = cs & (P - 1);
@@ -539,6 +576,7 @@ void decode_mfma_kernel(DecodeParams a) {
   Rec nxt = load_rec(it_begin);
   bool pre_issued = false;  // chunk 0 of the coming item is in kA / stage 0
   int pid_pre = 0;          // page ids (batch 0) of the coming item, when pre_issued
+  int pid_pre1 = 0;         // SMALLP: the lane's page id in chunk 1 of the coming item
   for (int it = it_begin; it < it_end; ++it) {
     const Rec cur = nxt;
     nxt = load_rec(it + 1);
@@ -548,7 +586,16 @@ void decode_mfma_kernel(DecodeParams a) {
     const int qrow = cur.qrow;
     const int nch = cx.nch;
     const int myn = nch > wave ? (nch - wave + kWaves - 1) / kWaves : 0;
-    int pid_vec = pre_issued ? pid_pre : load_pids(cx, 0);
+    int pid_vec = 0;
+    int idA = 0, idB = 0;  // SMALLP: the lane's page ids of the next even / odd chunk to issue
+    if constexpr (SMALLP) {
+      if (nch > 0) {
+        idA = load_id(cx, pre_issued ? 2 : 0);
+        idB = pre_issued ? pid_pre1 : load_id(cx, 1);
+      }
+    } else {
+      pid_vec = pre_issued ? pid_pre : load_pids(cx, 0);
+    }
 
     u32x4_t qp[NK];
     {
@@ -571,9 +618,16 @@ void decode_mfma_kernel(DecodeParams a) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) oacc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    // st (a constant at every call) is also the parity of kth
     auto issue_k = [&](int c, int kth, int st, u32x4_t (&kb)[NK]) {
-      if ((kth & 63) == 0 && kth > 0) pid_vec = load_pids(cx, kth >> 6);
-      issue(cx, pid_vec, c, kth, st, kb);
+      if constexpr (SMALLP) {
+        int& id = st ? idB : idA;
+        issue(cx, id, c, kth, st, kb);
+        id = load_id(cx, kth + 2);
+      } else {
+        if ((kth & 63) == 0 && kth > 0) pid_vec = load_pids(cx, kth >> 6);
+        issue(cx, pid_vec, c, kth, st, kb);
+      }
     };
 
     auto compute = [&](int c, int st, const u32x4_t (&kb)[NK]) {
@@ -630,8 +684,14 @@ void decode_mfma_kernel(DecodeParams a) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int dim = 16 * b + 4 * tr_sub;
-        const int piece = (dim >> 3) ^ (tr_tok & (NP - 1));
-        FI_LDS s16x4_t* src = (FI_LDS s16x4_t*)(stage + tr_tok * RB + piece * 16 + (dim & 7) * 2);
+        int off;
+        if constexpr (SMALLP) {  // piece pc of token t at (pc / 4) 1024 + (16 (pc % 4) + t) 16
+          const int pc = dim >> 3;
+          off = (pc >> 2) * 1024 + (16 * (pc & 3) + tr_tok) * 16;
+        } else {
+          off = tr_tok * RB + ((dim >> 3) ^ (tr_tok & (NP - 1))) * 16;
+        }
+        FI_LDS s16x4_t* src = (FI_LDS s16x4_t*)(stage + off + (dim & 7) * 2);
         const s16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(src);
         oacc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, bhi, oacc[b], 0, 0, 0);
         oacc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, blo, oacc[b], 0, 0, 0);
@@ -640,37 +700,48 @@ void decode_mfma_kernel(DecodeParams a) {
 
     const bool has_next = it + 1 < it_end;
     Ctx nx{0, 0, 0, 0, 0};
-    int pid_next = 0;
+    int pid_next = 0, pid_next1 = 0;
     {
       if (myn > 0 && !pre_issued) issue_k(wave, 0, 0, kA);
       for (int k = 0; k < myn; k += 2) {
         const bool n1 = k + 1 < myn;
         if (n1) issue_k(wave + kWaves * (k + 1), k + 1, 1, kB);
-        if (n1) FI_WAIT_VMCNT(2 * NK); else FI_WAIT_VMCNT(0);
+        if (n1) FI_WAIT_VMCNT(kChunkOps); else FI_WAIT_VMCNT(0);
         __builtin_amdgcn_sched_barrier(0);
         compute(wave + kWaves * k, 0, kA);
         __builtin_amdgcn_sched_barrier(0);
         if (k == 0 && has_next) {  // the next item's record has landed by now
           nx = make_ctx(nxt);
-          pid_next = load_pids(nx, 0);
+          if constexpr (SMALLP) {
+            pid_next = nx.nch > 0 ? load_id(nx, 0) : 0;
+            pid_next1 = nx.nch > 0 ? load_id(nx, 1) : 0;
+          } else {
+            pid_next = load_pids(nx, 0);
+          }
         }
         if (!n1) break;
         const bool n2 = k + 2 < myn;
         if (n2) issue_k(wave + kWaves * (k + 2), k + 2, 0, kA);
-        if (n2) FI_WAIT_VMCNT(2 * NK); else FI_WAIT_VMCNT(0);
+        if (n2) FI_WAIT_VMCNT(kChunkOps); else FI_WAIT_VMCNT(0);
         __builtin_amdgcn_sched_barrier(0);
         compute(wave + kWaves * (k + 1), 1, kB);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (myn == 0 && has_next) {
         nx = make_ctx(nxt);
-        pid_next = load_pids(nx, 0);
+        if constexpr (SMALLP) {
+          pid_next = nx.nch > 0 ? load_id(nx, 0) : 0;
+          pid_next1 = nx.nch > 0 ? load_id(nx, 1) : 0;
+        } else {
+          pid_next = load_pids(nx, 0);
+        }
       }
       // chunk 0 of the next item, into kA / stage 0 (this wave's last chunk
       // has been computed, so both are free)
       pre_issued = has_next && nx.nch > wave;
       if (pre_issued) {
         pid_pre = pid_next;
+        pid_pre1 = pid_next1;
         issue(nx, pid_pre, wave, 0, 0, kA);
       }
     }
@@ -719,10 +790,10 @@ void decode_mfma_kernel(DecodeParams a) {
   }
 }
 
-template <int D, int G, typename OT, bool ROPE>
+template <int D, int G, typename OT, bool ROPE, bool SMALLP>
 int launch_mfma(const RunArgs& r, const DecodeParams& p) {
   dim3 grid(r.workers, r.Hk), block(kThreads);
-  hipLaunchKernelGGL((decode_mfma_kernel<D, G, OT, ROPE>), grid, block, 0, (hipStream_t)r.hip_stream, p);
+  hipLaunchKernelGGL((decode_mfma_kernel<D, G, OT, ROPE, SMALLP>), grid, block, 0, (hipStream_t)r.hip_stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(FI_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return FI_OK;
@@ -741,7 +812,8 @@ int launch_t(const RunArgs& r, const DecodeParams& p) {
 template <typename T, int D, int G, typename OT, bool ROPE>
 int launch_fast(const RunArgs& r, const DecodeParams& p) {
   if constexpr (T::kBytes == 2) {
-    if (p.page_shift >= 0) return launch_mfma<D, G, OT, ROPE>(r, p);
+    if (p.page_shift >= 0) return launch_mfma<D, G, OT, ROPE, false>(r, p);
+    if (p.small_shift >= 0) return launch_mfma<D, G, OT, ROPE, true>(r, p);
   }
   return p.page_shift >= 0 ? launch_t<T, D, G, true, OT, ROPE>(r, p) : launch_t<T, D, G, false, OT, ROPE>(r, p);
 }
@@ -792,6 +864,12 @@ int launch_decode(const RunArgs& r) {
     int s = 0;
     while ((1 << s) < r.P) ++s;
     p.page_shift = s;
+  }
+  p.small_shift = -1;
+  if (r.P < 16 && (r.P & (r.P - 1)) == 0) {
+    int s = 0;
+    while ((1 << s) < r.P) ++s;
+    p.small_shift = s;
   }
   p.stream_at = r.stream_at;
   p.scale = r.sm_scale;
