@@ -39,6 +39,18 @@ int launch_prefill(const RunArgs& r) {
     while ((1 << sh) < r.P) ++sh;
     p.page_shift = sh;
   }
+  {
+    int sh = 0;
+    while ((2ll << sh) <= r.P) ++sh;  // floor(log2 P)
+    if ((r.P & (r.P - 1)) == 0) {
+      p.p_magic = 0u;
+      p.p_mask = 0xffffffffu;
+    } else {
+      p.p_magic = (uint32_t)((((uint64_t)1 << (32 + sh)) + (uint64_t)r.P - 1) / (uint64_t)r.P);
+      p.p_mask = 0u;
+    }
+    p.p_sh = sh;
+  }
   for (int i = 0; i < kRopeMaxPairs; ++i) p.rope_f[i] = r.rope_f[i];
   if (r.rope) return launch_prefill_rope(r, p);
   if (r.window >= 0) return launch_prefill_window(r, p);

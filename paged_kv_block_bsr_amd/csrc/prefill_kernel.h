@@ -62,6 +62,12 @@ struct PrefillParams {
   int32_t stream_at;
   int32_t workers;
   int32_t page_shift;  // log2(P) when P is a power of two >= 16, else -1
+  // key / P for any P as (umulhi(key, p_magic) + (key & p_mask)) >> p_sh
+  // (exact for keys below 2^31): a power of two has magic 0, mask all ones;
+  // any other P has sh = floor(log2 P), magic = ceil(2^(32 + sh) / P) < 2^32
+  uint32_t p_magic;
+  uint32_t p_mask;
+  int32_t p_sh;
   float scale_log2;
   float scale;
   float cap;
@@ -248,8 +254,12 @@ void prefill_kernel(PrefillParams a) {
   };
 
   // ---- staging
-  auto page_idx = [&](int key) { return FAST ? key >> a.page_shift : key / P; };
-  auto slot_of = [&](int key) { return FAST ? key & (P - 1) : key % P; };
+  auto page_idx = [&](int key) -> int {
+    if constexpr (FAST) return key >> a.page_shift;
+    const uint32_t k = (uint32_t)key;
+    return (int)((__umulhi(k, a.p_magic) + (k & a.p_mask)) >> a.p_sh);
+  };
+  auto slot_of = [&](int key) { return FAST ? key & (P - 1) : key - page_idx(key) * P; };
   auto clamp_key = [&](const Ctx& c, int key) { return key < c.t1 ? key : c.t1 - 1; };
   // page ids are loaded raw and checked where they are used, a tile
   // later, so the load is never waited for early; an id outside the pool

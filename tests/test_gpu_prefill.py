@@ -80,6 +80,40 @@ def test_prefill_sweep(D, G, P):
         assert_close(o, lse, o_ref, l_ref, f"prefill D={D} G={G} P={P} Wp={wp} br={br}")
 
 
+@pytest.mark.parametrize("P", [2, 5, 7, 8, 12, 100])
+def test_prefill_page_sizes(P):
+    """The general page path divides key positions by P with a multiply-high
+    and a shift (magic numbers from the host), for powers of two below 16
+    and for other sizes alike."""
+    seed = 700 + P
+    rng = np.random.default_rng(seed)
+    qo = [2, 17, int(rng.integers(2, 90)), 1, 0, 33, 130]
+    kv = [q + int(rng.integers(0, 3 * P + 70)) for q in qo]
+    kv[4] = 5
+    b = wl.make_batch(seed, qo, kv, page_size=P, num_qo_heads=8, num_kv_heads=2, head_dim=128,
+                      dtype=torch.bfloat16, causal=True, nan_poison=True)
+    o_ref, l_ref = ref.attention_of(b)
+    dev = DeviceBatch(b)
+    for wp, ms in ((1, 8), (5, 1)):
+        note(f"prefill page size P={P} Wp={wp}")
+        o, lse, _ = run(b, workers_decode=3, workers_prefill=wp, min_seg_pages=ms, dev=dev)
+        assert_close(o, lse, o_ref, l_ref, f"prefill P={P} Wp={wp}")
+
+
+def test_mixed_ragged_step_page_size_1_sampled():
+    """The mixed step stored one token per page, sampled rows at full size."""
+    m = wl.mixed_ragged_step()
+    b = wl.make_batch(1004, m.qo_lens, m.kv_lens, page_size=1, nan_poison=True)
+    note("mixed step P=1 gpu")
+    o, lse, plan = run(b)
+    assert plan.info.prefill_rows > 0 and plan.info.decode_rows == 48
+    rows = _rows_for(b)
+    note(f"mixed step P=1 oracle on {len(rows)} sampled rows")
+    o_ref, l_ref = ref.attention_rows_of(b, rows)
+    og, lg = _gather(o, lse, b, rows)
+    assert_close(og, lg, o_ref, l_ref, "mixed P=1 sampled")
+
+
 def test_prefill_non_causal_empty_cache_and_f32_out():
     b = wl.make_batch(41, [5, 40, 3], [0, 77, 9], page_size=16, num_qo_heads=8, num_kv_heads=2,
                       head_dim=128, dtype=torch.bfloat16, causal=False)
