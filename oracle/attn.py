@@ -21,6 +21,7 @@ _lib = None
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _f64p = ctypes.POINTER(ctypes.c_double)
+_u8p = ctypes.POINTER(ctypes.c_uint8)
 
 
 def lib():
@@ -44,13 +45,14 @@ def lib():
             L.oref_attention_rows.argtypes = [
                 ctypes.c_int, _i32p, _i32p, _i32p, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                 ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_int,
-                ctypes.c_double, ctypes.c_double, _f64p, _f64p, ctypes.c_int64, ctypes.c_int64,
-                _i32p, _i32p, _i32p, _f64p, _f64p]
+                ctypes.c_double, ctypes.c_double, _u8p, _i32p, _f64p, _f64p, ctypes.c_int64,
+                ctypes.c_int64, _i32p, _i32p, _i32p, _f64p, _f64p]
             L.oref_attention.restype = ctypes.c_int
             L.oref_attention.argtypes = [
                 ctypes.c_int, _i32p, _i32p, _i32p, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                 ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_int,
-                ctypes.c_double, ctypes.c_double, _f64p, _f64p, ctypes.c_int64, _f64p, _f64p]
+                ctypes.c_double, ctypes.c_double, _u8p, _i32p, _f64p, _f64p, ctypes.c_int64,
+                _f64p, _f64p]
             L.oref_merge_states.restype = ctypes.c_int
             L.oref_merge_states.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, _f64p,
                                             _f64p, _f64p, _f64p]
@@ -97,6 +99,17 @@ def validate(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, page_size, num_
                                head_dim, int(causal), int(pool_pages)))
 
 
+def _mask(tree_mask, mask_indptr):
+    """ctypes views of the optional tree mask (NULL pointers when absent)."""
+    if tree_mask is None:
+        return None, ctypes.cast(None, _u8p), None, ctypes.cast(None, _i32p)
+    tm = np.ascontiguousarray(np.asarray(tree_mask, dtype=np.uint8).reshape(-1))
+    if tm.size == 0:
+        tm = np.zeros(1, np.uint8)
+    mi = np.ascontiguousarray(np.asarray(mask_indptr, dtype=np.int32))
+    return tm, tm.ctypes.data_as(_u8p), mi, mi.ctypes.data_as(_i32p)
+
+
 def token_location(kv_indptr, kv_indices, page_size, request, token):
     """(page id, slot) of logical token ``token`` of request ``request``."""
     kp, kp_p = _i32(kv_indptr)
@@ -110,7 +123,7 @@ def token_location(kv_indptr, kv_indices, page_size, request, token):
 
 def attention(q, kv_pool, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, *, page_size,
               num_qo_heads, num_kv_heads, head_dim, causal, sm_scale, soft_cap=0.0,
-              window_left=-1, rope_theta=0.0, rope_scale=1.0):
+              window_left=-1, rope_theta=0.0, rope_scale=1.0, tree_mask=None, mask_indptr=None):
     """Exact attention for every query row.
 
     q: [total_qo, Hq, D]; kv_pool: [pages, 2, P, Hk, D]; qo_indptr None means
@@ -119,9 +132,14 @@ def attention(q, kv_pool, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, *,
     >= 0: the query at position kv_len - qo_len + t sees no key more than
     window_left positions before it.  rope_theta > 0: rotary embedding of q
     (at position kv_len - qo_len + t) and k (at position j), rotate-half form
-    with angle pos / rope_scale * rope_theta^(-2d/D).
+    with angle pos / rope_scale * rope_theta^(-2d/D).  tree_mask (uint8
+    bits, little-endian within a byte) with mask_indptr (bit offset of each
+    request's qo_len x qo_len block): draft token t sees draft token u <= t
+    iff bit t * qo_len + u is set (always itself), and every key before the
+    draft.
     """
     B = len(kv_indptr) - 1
+    tm, tm_p, mi, mi_p = _mask(tree_mask, mask_indptr)
     qa, q_p = _f64(q)
     pa, p_p = _f64(kv_pool)
     qo, qo_p = _i32(qo_indptr)
@@ -133,18 +151,20 @@ def attention(q, kv_pool, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, *,
     lse = np.zeros((total, num_qo_heads), np.float64)
     _check(lib().oref_attention(B, qo_p, kp_p, ki_p, kl_p, page_size, num_qo_heads, num_kv_heads,
                                 head_dim, int(causal), float(sm_scale), float(soft_cap),
-                                int(window_left), float(rope_theta), float(rope_scale), q_p, p_p,
-                                int(pa.shape[0]), o.ctypes.data_as(_f64p),
+                                int(window_left), float(rope_theta), float(rope_scale), tm_p, mi_p,
+                                q_p, p_p, int(pa.shape[0]), o.ctypes.data_as(_f64p),
                                 lse.ctypes.data_as(_f64p)))
     return o, lse
 
 
 def attention_rows(q, kv_pool, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, rows, *,
                    page_size, num_qo_heads, num_kv_heads, head_dim, causal, sm_scale,
-                   soft_cap=0.0, window_left=-1, rope_theta=0.0, rope_scale=1.0):
+                   soft_cap=0.0, window_left=-1, rope_theta=0.0, rope_scale=1.0, tree_mask=None,
+                   mask_indptr=None):
     """Exact attention for selected rows.  ``rows`` is an int array [n, 3] of
     (request, token-in-request, query head).  Returns (o [n, D], lse [n])."""
     B = len(kv_indptr) - 1
+    tm, tm_p, mi, mi_p = _mask(tree_mask, mask_indptr)
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 3))
     rq, rq_p = _i32(rows[:, 0].copy())
     rt, rt_p = _i32(rows[:, 1].copy())
@@ -161,7 +181,7 @@ def attention_rows(q, kv_pool, qo_indptr, kv_indptr, kv_indices, kv_last_page_le
     _check(lib().oref_attention_rows(B, qo_p, kp_p, ki_p, kl_p, page_size, num_qo_heads,
                                      num_kv_heads, head_dim, int(causal), float(sm_scale),
                                      float(soft_cap), int(window_left), float(rope_theta),
-                                     float(rope_scale), q_p, p_p, int(pa.shape[0]), n,
+                                     float(rope_scale), tm_p, mi_p, q_p, p_p, int(pa.shape[0]), n,
                                      rq_p, rt_p,
                                      rh_p, o.ctypes.data_as(_f64p), lse.ctypes.data_as(_f64p)))
     return o, lse
@@ -191,7 +211,8 @@ def attention_of(batch, **overrides):
               num_kv_heads=batch.num_kv_heads, head_dim=batch.head_dim, causal=batch.causal,
               sm_scale=batch.sm_scale, soft_cap=batch.soft_cap,
               window_left=getattr(batch, "window_left", -1),
-              rope_theta=getattr(batch, "rope_theta", 0.0), rope_scale=getattr(batch, "rope_scale", 1.0))
+              rope_theta=getattr(batch, "rope_theta", 0.0), rope_scale=getattr(batch, "rope_scale", 1.0),
+              tree_mask=getattr(batch, "tree_mask", None), mask_indptr=getattr(batch, "mask_indptr", None))
     kw.update(overrides)
     return attention(batch.q, batch.kv_pool, batch.qo_indptr, batch.kv_indptr, batch.kv_indices,
                      batch.kv_last_page_len, **kw)
@@ -202,7 +223,8 @@ def attention_rows_of(batch, rows, **overrides):
               num_kv_heads=batch.num_kv_heads, head_dim=batch.head_dim, causal=batch.causal,
               sm_scale=batch.sm_scale, soft_cap=batch.soft_cap,
               window_left=getattr(batch, "window_left", -1),
-              rope_theta=getattr(batch, "rope_theta", 0.0), rope_scale=getattr(batch, "rope_scale", 1.0))
+              rope_theta=getattr(batch, "rope_theta", 0.0), rope_scale=getattr(batch, "rope_scale", 1.0),
+              tree_mask=getattr(batch, "tree_mask", None), mask_indptr=getattr(batch, "mask_indptr", None))
     kw.update(overrides)
     return attention_rows(batch.q, batch.kv_pool, batch.qo_indptr, batch.kv_indptr,
                           batch.kv_indices, batch.kv_last_page_len, rows, **kw)

@@ -47,6 +47,18 @@
  *     rope_theta^(-2d/D), where the key j of a request sits at position j and
  *     the query t at kv_len - qo_len + t (the same alignment as the causal
  *     mask).  rope_scale <= 0 means 1.
+ *   - tree mask (paper page, opening paragraph: speculative decoding verifies
+ *     trees of guesses; "Customizable attention": a variant is a mask; the
+ *     token trees of speculative decoding on the serving-engine page): with a
+ *     mask given, the qo_len query tokens of a request are its draft tokens,
+ *     stored as its last qo_len keys (the bottom-right alignment of the
+ *     causal mask), and bit t * qo_len + u of the request's bit block
+ *     (starting at bit mask_indptr[i], row-major, bit b of byte k is bit
+ *     8 k + b) says whether draft token t sees draft token u.  Every query
+ *     sees all keys before the draft, always sees itself, and never sees a
+ *     later draft token (bits with u > t are ignored), so the mask only
+ *     narrows the causal one.  Needs causal = 1; requests with one query
+ *     ignore their bit.
  *
  * Parity pins: see the oracle tests (dense brute force, library SDPA, closed
  * forms, the pages' page-table example, page-permutation invariance,
@@ -166,16 +178,39 @@ static inline double pool_at(const double *pool, int64_t page, int kv, int64_t s
  * Attention for an explicit list of query rows (request, token-in-request,
  * query head).  o is [n_rows, D], lse is [n_rows].  q is [total_qo, Hq, D].
  */
+/* Whether draft token t of request i sees draft token u under the tree mask. */
+static int tree_bit(const uint8_t *mask, const int32_t *mask_indptr, int i, int64_t qo_len,
+                    int64_t t, int64_t u) {
+  if (u == t) return 1;
+  if (u > t) return 0;
+  const int64_t b = (int64_t)mask_indptr[i] + t * qo_len + u;
+  return (mask[b >> 3] >> (b & 7)) & 1;
+}
+
+/* Checks of the tree-mask arrays: causal, and qo_len^2 bits per request. */
+static int validate_mask(int B, const int32_t *qo_indptr, int causal, const int32_t *mask_indptr) {
+  if (!causal) return fail("a tree mask needs causal attention", 0, 0);
+  if (mask_indptr[0] != 0) return fail("mask_indptr[0] != 0", mask_indptr[0], 0);
+  for (int i = 0; i < B; ++i) {
+    const int64_t n = qo_len_of(qo_indptr, i);
+    if ((int64_t)mask_indptr[i + 1] - mask_indptr[i] != n * n)
+      return fail("mask_indptr step != qo_len^2", i, (int64_t)mask_indptr[i + 1] - mask_indptr[i]);
+  }
+  return OREF_OK;
+}
+
 int oref_attention_rows(int B, const int32_t *qo_indptr, const int32_t *kv_indptr,
                         const int32_t *kv_indices, const int32_t *kv_last_page_len, int P,
                         int Hq, int Hk, int D, int causal, double sm_scale, double soft_cap,
                         int window_left, double rope_theta, double rope_scale,
+                        const uint8_t *tree_mask, const int32_t *mask_indptr,
                         const double *q, const double *pool, int64_t pool_pages,
                         int64_t n_rows, const int32_t *row_req, const int32_t *row_tok,
                         const int32_t *row_head, double *o, double *lse) {
   int rc = oref_validate(B, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, P, Hq, Hk, D,
                          causal, pool_pages);
   if (rc) return rc;
+  if (tree_mask && (rc = validate_mask(B, qo_indptr, causal, mask_indptr))) return rc;
   const int rope = rope_theta > 0.0;
   if (rope && D % 2) return fail("rotary embedding needs an even head_dim", D, 0);
   if (rope_scale <= 0.0) rope_scale = 1.0;
@@ -220,9 +255,14 @@ int oref_attention_rows(int B, const int32_t *qo_indptr, const int32_t *kv_indpt
     double *kraw = qrot + D, *krot = qrot + 2 * D;
     if (rope) rope_rotate(qrow, qrot, D, (double)(kv_len - qo_len + t), rope_theta, rope_scale);
     const double *qv = rope ? qrot : qrow;
+    /* tree mask: draft keys (the last qo_len) outside the query's branch */
+    const int64_t draft0 = kv_len - qo_len;
+    const int masked = tree_mask && qo_len >= 2;
+#define OREF_HIDDEN(j) (masked && (j) >= draft0 && !tree_bit(tree_mask, mask_indptr, i, qo_len, t, (j) - draft0))
     /* pass 1: logits of every visible key, gathered one token at a time */
     double m = -INFINITY;
     for (int64_t j = first; j < limit; ++j) {
+      if (OREF_HIDDEN(j)) continue;
       int64_t page = kv_indices[kv_indptr[i] + j / P];
       int64_t slot = j % P;
       for (int d = 0; d < D; ++d) kraw[d] = pool_at(pool, page, 0, slot, g, d, P, Hk, D);
@@ -239,6 +279,7 @@ int oref_attention_rows(int B, const int32_t *qo_indptr, const int32_t *kv_indpt
     double z = 0.0;
     for (int d = 0; d < D; ++d) orow[d] = 0.0;
     for (int64_t j = first; j < limit; ++j) {
+      if (OREF_HIDDEN(j)) continue;
       int64_t page = kv_indices[kv_indptr[i] + j / P];
       int64_t slot = j % P;
       double w = exp(s[j - first] - m);
@@ -247,6 +288,7 @@ int oref_attention_rows(int B, const int32_t *qo_indptr, const int32_t *kv_indpt
     }
     for (int d = 0; d < D; ++d) orow[d] /= z;
     lse[r] = m + log(z);
+#undef OREF_HIDDEN
     free(s);
     free(qrot);
   }
@@ -259,7 +301,8 @@ int oref_attention_rows(int B, const int32_t *qo_indptr, const int32_t *kv_indpt
 int oref_attention(int B, const int32_t *qo_indptr, const int32_t *kv_indptr,
                    const int32_t *kv_indices, const int32_t *kv_last_page_len, int P, int Hq,
                    int Hk, int D, int causal, double sm_scale, double soft_cap, int window_left,
-                   double rope_theta, double rope_scale, const double *q, const double *pool,
+                   double rope_theta, double rope_scale, const uint8_t *tree_mask,
+                   const int32_t *mask_indptr, const double *q, const double *pool,
                    int64_t pool_pages, double *o, double *lse) {
   int64_t total = 0;
   for (int i = 0; i < B; ++i) total += qo_len_of(qo_indptr, i);
@@ -279,7 +322,7 @@ int oref_attention(int B, const int32_t *qo_indptr, const int32_t *kv_indptr,
       }
   int rc = oref_attention_rows(B, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, P, Hq, Hk,
                                D, causal, sm_scale, soft_cap, window_left, rope_theta, rope_scale,
-                               q, pool, pool_pages, n,
+                               tree_mask, mask_indptr, q, pool, pool_pages, n,
                                rq, rt, rh, o, lse);
   free(rq); free(rt); free(rh);
   return rc;

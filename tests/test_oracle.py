@@ -582,3 +582,129 @@ def test_rope_logits_depend_only_on_relative_positions():
     # window alone decides; with a different key set the outputs differ
     on, ln = ref.attention_of(a, window_left=w)
     assert not np.allclose(on, oa, atol=1e-6)
+
+
+# ---- tree mask (speculative decoding: the draft tokens are the request's
+# last qo_len keys; draft token t sees the keys before the draft, itself and
+# the draft tokens whose bit (t, u) is set, never a later one)
+# --------------------------------------------------------------------------
+
+def _tree_batch(seed, qo, kv, P, cap=0.0, D=8):
+    import workloads as wl
+    b = wl.make_batch(seed, qo, kv, page_size=P, num_qo_heads=4, num_kv_heads=2, head_dim=D,
+                      dtype=torch.float32, causal=True, soft_cap=cap)
+    rng = np.random.default_rng(seed + 1)
+    parents = [wl.random_tree_parents(rng, int(n), max_children=2) for n in qo]
+    b.tree_mask, b.mask_indptr = wl.tree_mask_bits(parents, qo)
+    return b, parents
+
+
+def _lower_block(qo, fill):
+    """Bits of per-request qo x qo blocks from a function fill(i, t, u)."""
+    bits = []
+    for i, n in enumerate(qo):
+        for t in range(n):
+            for u in range(n):
+                bits.append(bool(fill(i, t, u)))
+    ind = np.zeros(len(qo) + 1, np.int32)
+    ind[1:] = np.cumsum([n * n for n in qo])
+    return np.packbits(np.array(bits, bool), bitorder="little"), ind
+
+
+def test_tree_mask_of_the_whole_lower_triangle_is_causal():
+    b, _ = _tree_batch(601, [5, 1, 9, 3], [20, 7, 9, 30], 4, cap=6.0)
+    qo = [5, 1, 9, 3]
+    bits, ind = _lower_block(qo, lambda i, t, u: u <= t)
+    o0, l0 = ref.attention_of(b, tree_mask=None, mask_indptr=None)
+    o1, l1 = ref.attention_of(b, tree_mask=bits, mask_indptr=ind)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_tree_mask_ignores_bits_above_the_diagonal():
+    b, _ = _tree_batch(602, [6, 4], [30, 4], 3)
+    qo = [6, 4]
+    rng = np.random.default_rng(7)
+    r = rng.random((2, 6, 6)) < 0.5
+    full, ind = _lower_block(qo, lambda i, t, u: r[i, t, u])
+    low, _ = _lower_block(qo, lambda i, t, u: r[i, t, u] and u <= t)
+    o0, l0 = ref.attention_of(b, tree_mask=full, mask_indptr=ind)
+    o1, l1 = ref.attention_of(b, tree_mask=low, mask_indptr=ind)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_tree_mask_single_query_requests_ignore_their_bit():
+    import workloads as wl
+    b = wl.make_batch(603, [1, 1, 1], [9, 1, 40], page_size=4, num_qo_heads=4, num_kv_heads=2,
+                      head_dim=8, dtype=torch.float32, causal=True)
+    o0, l0 = ref.attention_of(b)
+    zero = np.zeros(1, np.uint8)
+    o1, l1 = ref.attention_of(b, tree_mask=zero, mask_indptr=np.array([0, 1, 2, 3], np.int32))
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+@pytest.mark.parametrize("cap", [0.0, 5.0])
+def test_tree_mask_equals_dense_attention_over_prefix_and_ancestors(cap):
+    """Brute force per query row: dense softmax over exactly the keys before
+    the draft, the row's own key and its ancestors' keys (walked from the
+    parent array, not from the bits)."""
+    qo = [7, 2, 12, 1, 5]
+    kv = [19, 2, 40, 6, 5]
+    b, parents = _tree_batch(604, qo, kv, 4, cap=cap)
+    o, lse = ref.attention_of(b)
+    qi = b.qo_indptr
+    for i in range(len(qo)):
+        K, V = _keys_of(b, i)
+        L, n = K.shape[0], qo[i]
+        d0 = L - n
+        for t in range(n):
+            keep = list(range(d0))
+            u = t
+            while u >= 0:
+                keep.append(d0 + u)
+                u = int(parents[i][u])
+            keep = np.array(sorted(keep))
+            Q = b.q[qi[i] + t:qi[i] + t + 1].double().numpy()
+            o_d, l_d = dense_ref(Q, K[keep].astype(np.float64), V[keep].astype(np.float64),
+                                 b.sm_scale, cap, causal=False)
+            assert np.allclose(o[qi[i] + t], o_d[0], rtol=0, atol=1e-12), (i, t)
+            assert np.allclose(lse[qi[i] + t], l_d[0], rtol=0, atol=1e-12), (i, t)
+
+
+def test_tree_mask_with_no_bits_sees_the_prefix_and_itself():
+    qo = [4, 6]
+    kv = [4, 13]
+    b, _ = _tree_batch(605, qo, kv, 2)
+    bits, ind = _lower_block(qo, lambda i, t, u: False)
+    o, lse = ref.attention_of(b, tree_mask=bits, mask_indptr=ind)
+    qi = b.qo_indptr
+    for i in range(2):
+        K, V = _keys_of(b, i)
+        d0 = K.shape[0] - qo[i]
+        for t in range(qo[i]):
+            keep = np.array(list(range(d0)) + [d0 + t])
+            Q = b.q[qi[i] + t:qi[i] + t + 1].double().numpy()
+            o_d, l_d = dense_ref(Q, K[keep].astype(np.float64), V[keep].astype(np.float64),
+                                 b.sm_scale, 0.0, causal=False)
+            assert np.allclose(o[qi[i] + t], o_d[0], rtol=0, atol=1e-12)
+            assert np.allclose(lse[qi[i] + t], l_d[0], rtol=0, atol=1e-12)
+
+
+def test_tree_mask_is_invariant_under_page_permutation():
+    b, _ = _tree_batch(606, [9, 3], [25, 11], 4)
+    o0, l0 = ref.attention_of(b)
+    rng = np.random.default_rng(8)
+    sigma = rng.permutation(b.pool_pages)
+    pool2 = torch.empty_like(b.kv_pool)
+    pool2[torch.from_numpy(sigma)] = b.kv_pool
+    b.kv_pool = pool2
+    b.kv_indices = sigma[b.kv_indices].astype(np.int32)
+    o1, l1 = ref.attention_of(b)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_tree_mask_rejects_non_causal_and_bad_offsets():
+    b, _ = _tree_batch(607, [3, 2], [5, 9], 4)
+    with pytest.raises(ref.OracleError):
+        ref.attention_of(b, causal=False)
+    with pytest.raises(ref.OracleError):
+        ref.attention_of(b, mask_indptr=np.array([0, 9, 12], np.int32))

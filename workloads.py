@@ -61,6 +61,8 @@ class PagedBatch:
     name: str = ""
     meta: dict = field(default_factory=dict)
     window_left: int = -1          # sliding window (keys before the query's own); -1 = none
+    tree_mask: Optional[np.ndarray] = None    # uint8 bits (speculative-decoding token trees); None = none
+    mask_indptr: Optional[np.ndarray] = None  # int32 [B+1]: bit offset of request i's qo x qo block
 
     @property
     def batch_size(self) -> int:
@@ -293,3 +295,61 @@ WORKLOADS = {
     "mixed_ragged_step": mixed_ragged_step,
     "shared_prefix_cascade": shared_prefix_cascade,
 }
+
+
+# --------------------------------------------------------------------------
+# Token trees of speculative decoding (input structure only).
+# --------------------------------------------------------------------------
+
+def random_tree_parents(rng: np.random.Generator, n: int, max_children: int = 4) -> np.ndarray:
+    """Parent of each of n draft tokens in topological order: token 0 is the
+    root (parent -1); token t > 0 hangs under a random earlier token that has
+    fewer than ``max_children`` children."""
+    parent = np.full(n, -1, np.int64)
+    kids = np.zeros(n, np.int64)
+    for t in range(1, n):
+        while True:
+            p = int(rng.integers(0, t))
+            if kids[p] < max_children:
+                break
+        parent[t] = p
+        kids[p] += 1
+    return parent
+
+
+def tree_mask_bits(parents_per_request, qo_lens):
+    """Pack per-request ancestor masks: bit t * n + u of request i's block is
+    set iff draft token u is token t or one of its ancestors.  Returns (bits
+    as uint8, little-endian within a byte; mask_indptr int32 [B+1] of bit
+    offsets).  A request with qo_len <= 1 gets its qo_len^2 bits set."""
+    blocks = []
+    for par, n in zip(parents_per_request, qo_lens):
+        n = int(n)
+        m = np.zeros((n, n), bool)
+        for t in range(n):
+            u = t
+            while u >= 0:
+                m[t, u] = True
+                u = int(par[u]) if par is not None else -1
+        blocks.append(m.reshape(-1))
+    flat = np.concatenate(blocks) if blocks else np.zeros(0, bool)
+    indptr = np.zeros(len(blocks) + 1, np.int32)
+    indptr[1:] = np.cumsum([b.size for b in blocks])
+    return np.packbits(flat, bitorder="little"), indptr
+
+
+def speculative_verify(seed: int = 1006, num_requests: int = 32, draft_lens=(16, 32, 64),
+                       prefix_range=(512, 4096), page_size=16, nan_poison=False) -> PagedBatch:
+    """Speculative-decoding verification step: each request checks a random
+    draft token tree of 16, 32 or 64 tokens on top of a cached prefix
+    (uniform in [512, 4096]); 32/8 heads, D = 128, bf16, page 16.  The draft
+    tokens are the request's last keys; the tree mask lets each one see its
+    ancestors."""
+    rng = np.random.default_rng(seed)
+    qo = rng.choice(np.asarray(draft_lens), size=num_requests).astype(np.int64)
+    prefix = rng.integers(prefix_range[0], prefix_range[1], size=num_requests, endpoint=True)
+    parents = [random_tree_parents(rng, int(n)) for n in qo]
+    b = make_batch(seed, qo, prefix + qo, page_size=page_size, nan_poison=nan_poison,
+                   name="speculative_verify")
+    b.tree_mask, b.mask_indptr = tree_mask_bits(parents, qo)
+    return b
