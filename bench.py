@@ -192,6 +192,19 @@ def prefill_flops(b, window_left=-1) -> int:
     return 4 * b.head_dim * b.num_qo_heads * tot
 
 
+def tree_flops(b) -> int:
+    """Visible flops under a tree mask: 4 D per (query head, visible key)
+    pair, where draft token t sees the keys before the draft, itself and the
+    draft tokens its bits name (u < t)."""
+    bits = np.unpackbits(np.asarray(b.tree_mask, np.uint8), bitorder="little")
+    tot = 0
+    for i, (qo, kv) in enumerate(zip(b.qo_lens.tolist(), b.kv_lens.tolist())):
+        blk = bits[b.mask_indptr[i]:b.mask_indptr[i] + qo * qo].reshape(qo, qo).astype(bool)
+        vis = np.tril(blk, -1).sum(axis=1) + 1 + (kv - qo)
+        tot += int(vis.sum())
+    return 4 * b.head_dim * b.num_qo_heads * tot
+
+
 def prefill_slice(b):
     """The batch restricted to its multi-query requests (same pool and values)."""
     import workloads as wl
@@ -239,8 +252,14 @@ def time_batch_call(b, steps, warmup, workers_decode=0, workers_prefill=0, pool_
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
     ws = torch.empty(plan.float_ws_bytes // 4 + 64, dtype=torch.float32, device=dev)
+    mask = mask_ip = None
+    if getattr(b, "tree_mask", None) is not None:
+        mask = torch.from_numpy(fi.tree_mask_words(b.tree_mask)).to(dev)
+        mask_ip = i32(b.mask_indptr)
     params = fi.make_params(b.dtype, b.dtype, b.num_qo_heads, Hk, b.head_dim, b.page_size,
-                            b.sm_scale, b.soft_cap, rope_theta=rope_theta)
+                            b.sm_scale, b.soft_cap, rope_theta=rope_theta, tree_mask=mask,
+                            mask_indptr=mask_ip,
+                            mask_bits=0 if mask is None else int(b.mask_indptr[-1]))
     qo_d, kvp_d, kvi_d, last_d = (None if b.qo_indptr is None else i32(b.qo_indptr),
                                   i32(b.kv_indptr), i32(b.kv_indices), i32(b.kv_last_page_len))
 
@@ -294,6 +313,16 @@ def secondary_measurements(args):
     out["window"] = window_measurements(ps, args.side_steps)
     out["rope"] = rope_measurements(ps, args.side_steps)
     del b, ps
+    sv = wl.speculative_verify()
+    ms, plan = time_batch_call(sv, args.side_steps, 3)
+    fl = tree_flops(sv)
+    out["tree_mask"] = {"workload": "speculative_verify (32 requests, draft trees of 16/32/64 tokens "
+                                    "over prefixes U[512, 4096], tree mask)",
+                        "ms": round(ms, 4), "flops": fl, "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                        "frac": round(fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                        "bytes": decode_bytes(sv),
+                        "gbs": round(decode_bytes(sv) / (ms * 1e-3) / 1e9, 1)}
+    del sv
     cb = wl.shared_prefix_cascade()
     ms_flat, _ = time_batch_call(cb.flat, args.side_steps, 3)
     ms_casc = time_cascade(cb, args.side_steps, 3)

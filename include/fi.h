@@ -179,6 +179,27 @@ typedef struct fi_attn_params {
   int32_t graph_safe;
   float rope_theta;
   float rope_scale;
+  /* Tree mask of speculative decoding (paper page, opening paragraph: trees
+   * of guesses verified by speculative decoding; serving-engine page, token
+   * trees among the KV layouts), fi_batch_prefill_paged only; NULL = none.
+   * The qo_len query tokens of request i are its draft tokens, stored as its
+   * last qo_len keys (the bottom-right alignment of the causal mask).  Bit
+   * t * qo_len + u of the request's block, which starts at bit
+   * mask_indptr[i] of the stream, lets draft token t see draft token u.  A
+   * query always sees the keys before the draft and its own key, never a
+   * later draft token (bits with u > t are ignored); a request with one
+   * query ignores its bit.  Needs a causal plan without a sliding window and
+   * no rotary embedding (else FI_ERR_UNSUPPORTED).
+   *   tree_mask    device uint32 words; bit n of the stream is bit n % 32 of
+   *                word n / 32 (the little-endian bit order of a byte array
+   *                padded to whole words); holds ceil(mask_bits / 32) words
+   *   mask_indptr  device int32 [batch + 1]: mask_indptr[0] = 0 and
+   *                mask_indptr[i + 1] - mask_indptr[i] = qo_len_i^2 (not
+   *                checked on the device; bits past mask_bits are not read)
+   *   mask_bits    total bits, mask_indptr[batch]; 1 <= mask_bits < 2^31 */
+  const uint32_t* tree_mask;
+  const int32_t* mask_indptr;
+  int64_t mask_bits;
 } fi_attn_params;
 
 /*

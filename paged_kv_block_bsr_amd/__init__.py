@@ -26,4 +26,5 @@ from .binding import (  # noqa: F401
     fi_version,
     lib,
     make_params,
+    tree_mask_words,
 )

@@ -87,7 +87,10 @@ class fi_attn_params(ctypes.Structure):
                 ("logits_soft_cap", ctypes.c_float),
                 ("graph_safe", ctypes.c_int32),
                 ("rope_theta", ctypes.c_float),
-                ("rope_scale", ctypes.c_float)]
+                ("rope_scale", ctypes.c_float),
+                ("tree_mask", ctypes.c_void_p),
+                ("mask_indptr", ctypes.c_void_p),
+                ("mask_bits", ctypes.c_int64)]
 
 
 _lib = None
@@ -236,15 +239,31 @@ def fi_plan_bounds(batch_size, total_qo, num_qo_heads, num_kv_heads, head_dim, w
 
 
 def make_params(q_dtype, out_dtype, num_qo_heads, num_kv_heads, head_dim, page_size, sm_scale=0.0,
-                logits_soft_cap=0.0, graph_safe=False, rope_theta=0.0, rope_scale=1.0) -> fi_attn_params:
+                logits_soft_cap=0.0, graph_safe=False, rope_theta=0.0, rope_scale=1.0,
+                tree_mask=None, mask_indptr=None, mask_bits=0) -> fi_attn_params:
     """``graph_safe``: launch every kernel of a call whatever the plan, so a
     call captured into a graph stays valid for later plans of the same shapes.
     ``rope_theta`` > 0: fused rotary embedding of q and k (``rope_scale``
-    divides the positions)."""
+    divides the positions).  ``tree_mask`` (device int32 / uint32 words of
+    the bit stream, see :func:`tree_mask_words`), ``mask_indptr`` (device
+    int32) and ``mask_bits``: the speculative-decoding tree mask of a prefill
+    call.  The params hold raw device addresses: keep those tensors alive
+    while the params are used."""
     return fi_attn_params(_dtype_code(q_dtype), _dtype_code(out_dtype), num_qo_heads,
                           num_kv_heads, head_dim, page_size, float(sm_scale),
                           float(logits_soft_cap), int(bool(graph_safe)), float(rope_theta),
-                          float(rope_scale))
+                          float(rope_scale), _ptr(tree_mask) if tree_mask is not None else None,
+                          _ptr(mask_indptr) if mask_indptr is not None else None, int(mask_bits))
+
+
+def tree_mask_words(bits_u8) -> np.ndarray:
+    """A little-endian byte stream of mask bits as int32 words (padded with
+    zero bytes to whole words), the layout the tree-mask parameter takes."""
+    b = np.asarray(bits_u8, dtype=np.uint8).reshape(-1)
+    pad = (-b.size) % 4
+    if pad or b.size == 0:
+        b = np.concatenate([b, np.zeros(pad if b.size else 4, np.uint8)])
+    return b.view(np.int32).copy()
 
 
 def fi_batch_decode_paged(plan: Plan, plan_dev, params: fi_attn_params, q, kv_pool,

@@ -46,6 +46,14 @@ int check_params(const fi_attn_params* p) {
     return set_error(FI_ERR_INVALID_ARG, "sm_scale / logits_soft_cap");
   if (!std::isfinite(p->rope_theta) || !std::isfinite(p->rope_scale))
     return set_error(FI_ERR_INVALID_ARG, "rope_theta / rope_scale");
+  if (p->tree_mask) {
+    if (!p->mask_indptr || p->mask_bits < 1 || p->mask_bits >= ((int64_t)1 << 31))
+      return set_error(FI_ERR_INVALID_ARG, "tree mask: null mask_indptr or mask_bits outside [1, 2^31)");
+    if (reinterpret_cast<uintptr_t>(p->tree_mask) & 3u)
+      return set_error(FI_ERR_INVALID_ARG, "tree mask: words must be 4-byte aligned");
+    if (p->rope_theta > 0.f)
+      return set_error(FI_ERR_UNSUPPORTED, "tree mask with the rotary embedding");
+  }
   return FI_OK;
 }
 
@@ -112,6 +120,9 @@ RunArgs base_args(const int32_t* plan_dev, const fi_attn_params* p, const void* 
   a.causal = ph[H_CAUSAL];
   a.window = ph[H_WINDOW];
   rope_table(p, a);
+  a.mask = p->tree_mask;
+  a.mask_indptr = p->mask_indptr;
+  a.mask_last_word = p->tree_mask ? (int32_t)((p->mask_bits - 1) >> 5) : 0;
   a.sm_scale = resolve_scale(p);
   a.soft_cap = p->logits_soft_cap;
   a.dtype = p->dtype;
@@ -219,6 +230,8 @@ int fi_batch_prefill_paged(const int32_t* plan_host, const int32_t* plan_dev,
   if (rc) return rc;
   if (plan_host[H_BATCH] > 0 && !qo_indptr)
     return set_error(FI_ERR_INVALID_ARG, "fi_batch_prefill_paged: null qo_indptr");
+  if (params->tree_mask && (plan_host[H_CAUSAL] != 1 || plan_host[H_WINDOW] >= 0))
+    return set_error(FI_ERR_UNSUPPORTED, "fi_batch_prefill_paged: a tree mask needs a causal plan without a window");
   RunArgs a = base_args(plan_dev, params, q, kv_pool, pool_pages, qo_indptr, kv_indptr, kv_indices,
                         kv_last_page_len, o, lse, float_ws, params->out_dtype, plan_host, stream);
   return run_plan(a, plan_host, true, params->graph_safe != 0);
@@ -266,6 +279,7 @@ int fi_cascade(const int32_t* plan0_host, const int32_t* plan0_dev, const int32_
     return set_error(FI_ERR_PLAN_MISMATCH, "fi_cascade: level-0 plan must be non-causal");
   if (params->rope_theta > 0.f)
     return set_error(FI_ERR_UNSUPPORTED, "fi_cascade: the rotary embedding is not supported");
+  if (params->tree_mask) return set_error(FI_ERR_UNSUPPORTED, "fi_cascade: tree masks are not supported");
   if (plan0_host[H_WINDOW] >= 0 || plan1_host[H_WINDOW] >= 0)
     return set_error(FI_ERR_UNSUPPORTED, "fi_cascade: plans with a sliding window are not supported");
   if (plan0_host[H_TOTAL_QO] != plan1_host[H_TOTAL_QO])

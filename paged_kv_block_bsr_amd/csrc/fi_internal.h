@@ -35,6 +35,9 @@ struct RunArgs {
   int32_t causal;
   int32_t window;               // sliding window (keys before the query's own); -1 = none
   int32_t rope;                 // rotary embedding on q and k (rope_f holds its table)
+  const uint32_t* mask;         // tree mask words, or NULL (prefill kernels only)
+  const int32_t* mask_indptr;   // bit offset of each request's qo x qo block
+  int32_t mask_last_word;       // index of the mask's last word
   uint32_t rope_f[64];          // per pair d < D/2: turn per position, 2^-32 revolutions
   float sm_scale;
   float soft_cap;

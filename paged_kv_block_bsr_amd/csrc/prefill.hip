@@ -52,6 +52,10 @@ int launch_prefill(const RunArgs& r) {
     p.p_sh = sh;
   }
   for (int i = 0; i < kRopeMaxPairs; ++i) p.rope_f[i] = r.rope_f[i];
+  p.mask = r.mask;
+  p.mask_indptr = r.mask_indptr;
+  p.mask_last_word = r.mask_last_word;
+  if (r.mask) return launch_prefill_mask(r, p);
   if (r.rope) return launch_prefill_rope(r, p);
   if (r.window >= 0) return launch_prefill_window(r, p);
   return launch_mode<false, false>(r, p);

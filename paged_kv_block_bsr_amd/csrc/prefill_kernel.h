@@ -37,6 +37,12 @@
 //     the S^T registers.  P and V run in fp16: bf16 V converts exactly in
 //     fp16's normal range (the conversion saturates at +-65504), and fp16
 //     keeps 11 bits of P where bf16 keeps 8.
+//   - with a tree mask (MASK, speculative decoding: paper page, opening
+//     paragraph, and the token trees of the serving-engine page), the
+//     request's draft tokens are its last qo_len keys; tiles that reach the
+//     draft take the masked step, where each lane tests the bits of its row
+//     (two 32-bit words per 32-key block, loaded before the step's K/V
+//     loads) for the draft keys of the block.
 #pragma once
 #include <type_traits>
 
@@ -73,6 +79,11 @@ struct PrefillParams {
   float cap;
   float inv_cap;
   int32_t window;      // sliding window: keys seen before the query's own (kernels built with WIN)
+  // tree mask (kernels built with MASK): bit n of the bit stream is bit n % 32
+  // of mask[n / 32]; request i's qo x qo block starts at bit mask_indptr[i]
+  const uint32_t* mask;
+  const int32_t* mask_indptr;
+  int32_t mask_last_word;
   uint32_t rope_f[kRopeMaxPairs];  // rotary turn per position of pair d (kernels built with ROPE)
 };
 
@@ -140,7 +151,7 @@ struct PShape {
   static constexpr int VThreads = 16 * VPiecesRow;             // threads staging V: 4 keys x 1 piece each
 };
 
-template <int D, int G, bool FAST, bool CAP, bool WIN, bool ROPE, typename OT>
+template <int D, int G, bool FAST, bool CAP, bool WIN, bool ROPE, bool MASK, typename OT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillParams a) {
   using SH = PShape<D>;
@@ -217,14 +228,14 @@ void prefill_kernel(PrefillParams a) {
   // before that item's epilogue: consecutive items of a worker overlap
   // instead of paying three dependent memory round trips each.
   struct Item {
-    int pb, pe, slot, rb, re, kvb, kv_len, qbase, qo_len;
+    int pb, pe, slot, rb, re, kvb, kv_len, qbase, qo_len, req;
   };
   auto load_item = [&](int it) -> Item {
-    Item x{0, 0, -1, 0, 0, 0, 0, 0, 0};  // past the worker's last item: no keys
+    Item x{0, 0, -1, 0, 0, 0, 0, 0, 0, 0};  // past the worker's last item: no keys
     if (it < it_end) {
       const int32_t* im = meta + kMetaInts * it;
       x = Item{items[4 * it + 1], items[4 * it + 2], items[4 * it + 3], im[M_RB], im[M_RE],
-               im[M_KVB],         im[M_KVLEN],       im[M_QOBASE],      im[M_QOLEN]};
+               im[M_KVB],         im[M_KVLEN],       im[M_QOBASE],      im[M_QOLEN], MASK ? im[M_REQ] : 0};
     }
     return x;
   };
@@ -233,7 +244,7 @@ void prefill_kernel(PrefillParams a) {
   // conversion does not wait for them)
   auto uniform = [](const Item& x) {
     auto u = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
-    return Item{u(x.pb), u(x.pe), u(x.slot), u(x.rb), u(x.re), u(x.kvb), u(x.kv_len), u(x.qbase), u(x.qo_len)};
+    return Item{u(x.pb), u(x.pe), u(x.slot), u(x.rb), u(x.re), u(x.kvb), u(x.kv_len), u(x.qbase), u(x.qo_len), u(x.req)};
   };
   // an item's keys [t0, t1) in ntiles tiles, and its request's page ids
   struct Ctx {
@@ -443,6 +454,11 @@ void prefill_kernel(PrefillParams a) {
     // well inside int32).  The lane holds lo instead of lim: a causal row's
     // key limit is lo + w + 1 (unless lo was clamped, and then it sees no key
     // of the item), a non-causal one's is the item's end.
+    // Tree mask: the first bit of this lane's row (draft token tok of a
+    // request whose draft starts at key causal_off); read in masked steps,
+    // where the compiler waits for it.
+    int mrow = 0;
+    if constexpr (MASK) mrow = a.mask_indptr[item.req] + tok * item.qo_len;
     int lo = 0, wave_lo_max = 0, w = 0;
     if constexpr (WIN) {
       w = min(a.window, item.kv_len);
@@ -502,7 +518,7 @@ void prefill_kernel(PrefillParams a) {
     // key limit (tiles that reach past the wave's smallest limit); 2 the
     // limit and the window start (tiles that start before the wave's largest
     // window start)
-    auto prepare = [&](int n, int b, f32x16_t& s, auto mask_tag) {
+    auto prepare = [&](int n, int b, f32x16_t& s, auto mask_tag, uint64_t mwin) {
       constexpr int M = decltype(mask_tag)::value;
       const int bs = t0 + n * kTileK + 32 * b;
       if constexpr (CAP) {
@@ -530,7 +546,29 @@ void prefill_kernel(PrefillParams a) {
           if constexpr (M == 1) s[e] = kk < rel ? s[e] : neg_inf();
           else s[e] = (uint32_t)(kk - rlo) < (uint32_t)(rel - rlo) ? s[e] : neg_inf();
         }
+        if constexpr (MASK) {
+          // draft key u = key - causal_off (u < 0: a key before the draft,
+          // visible; u == tok: the row's own key, visible): bit mrow + u,
+          // at bit mrow + u - 32 w0 of the block's 64-bit window
+          const int ub = bs + 4 * hh - causal_off;  // u of the lane's first key in the block
+          const int w0 = (mrow + max(ub, 0)) >> 5;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int u = ub + 8 * (e >> 2) + (e & 3);
+            const bool vis = u < 0 || u == tok || ((mwin >> ((mrow + u - 32 * w0) & 63)) & 1ull);
+            s[e] = vis ? s[e] : neg_inf();
+          }
+        }
       }
+    };
+    // the two words of a block's mask window (see prepare); the word index
+    // is clamped to the stream's last word, past which no bit is read
+    auto mask_window = [&](int n, int b) -> uint64_t {
+      const int ub = t0 + n * kTileK + 32 * b + 4 * hh - causal_off;
+      const int w0 = (mrow + max(ub, 0)) >> 5;
+      const uint32_t lo_w = a.mask[min(w0, a.mask_last_word)];
+      const uint32_t hi_w = a.mask[min(w0 + 1, a.mask_last_word)];
+      return (uint64_t)lo_w | ((uint64_t)hi_w << 32);
     };
     // Online softmax of a prepared block, in two parts.  update_max: the
     // block's row max; the running max moves only when a block beats it by
@@ -616,6 +654,11 @@ void prefill_kernel(PrefillParams a) {
       u32x4_t vop0[2][SH::DBlocks], vop1[2][SH::DBlocks];
       f32x16_t s0, s1;
       f16x8_t p0[2], p1[2];
+      uint64_t mw0 = 0, mw1 = 0;
+      if constexpr (MASK && decltype(mask_tag)::value >= 1) {  // before the tile loads, so that their use waits for these alone
+        mw0 = mask_window(n, 0);
+        mw1 = mask_window(n, 1);
+      }
       kread(kb, 0, kop0);
       kread(kb, 1, kop1);
       dma_k(cx, n + 1, kb_next, pk);
@@ -623,13 +666,13 @@ void prefill_kernel(PrefillParams a) {
       pk = fetch_k(cx, n + 2);
       pv_ids = fetch_v(cx, n + 2);
       qk(kop0, s0);
-      prepare(n, 0, s0, mask_tag);
+      prepare(n, 0, s0, mask_tag, mw0);
       // QK(b1) + softmax(b0) + V(b0) reads
       qk(kop1, s1);
       update_max(s0);
       vread(vb, 0, vop0);
       exps(s0, p0);
-      prepare(n, 1, s1, mask_tag);
+      prepare(n, 1, s1, mask_tag, mw1);
       // PV(b0) + softmax(b1) + V(b1) reads
       pv(vop0, p0);
       update_max(s1);
@@ -649,7 +692,8 @@ void prefill_kernel(PrefillParams a) {
     };
     auto step_any = [&](int n, auto cur) {
       const int ts = t0 + n * kTileK;
-      if (ts + kTileK > wave_lim_min || (WIN && ts < wave_lo_max)) step(n, cur, std::integral_constant<int, WIN ? 2 : 1>{});
+      if (ts + kTileK > wave_lim_min || (WIN && ts < wave_lo_max) || (MASK && ts + kTileK > causal_off))
+        step(n, cur, std::integral_constant<int, WIN ? 2 : 1>{});
       else step(n, cur, std::integral_constant<int, 0>{});
     };
     for (int n = 0; n < ntiles; n += 2) {
@@ -716,51 +760,52 @@ void prefill_kernel(PrefillParams a) {
   }
 }
 
-template <int D, int G, bool FAST, bool CAP, bool WIN, bool ROPE, typename OT>
+template <int D, int G, bool FAST, bool CAP, bool WIN, bool ROPE, bool MASK, typename OT>
 int launch_k(const RunArgs& r, const PrefillParams& p) {
   dim3 grid(r.workers * r.Hk), block(kThreads);
-  hipLaunchKernelGGL((prefill_kernel<D, G, FAST, CAP, WIN, ROPE, OT>), grid, block, 0, (hipStream_t)r.hip_stream, p);
+  hipLaunchKernelGGL((prefill_kernel<D, G, FAST, CAP, WIN, ROPE, MASK, OT>), grid, block, 0, (hipStream_t)r.hip_stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(FI_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
   return FI_OK;
 }
 
-template <int D, int G, bool WIN, bool ROPE, typename OT>
+template <int D, int G, bool WIN, bool ROPE, bool MASK, typename OT>
 int launch_t(const RunArgs& r, const PrefillParams& p) {
   const bool fast = p.page_shift >= 0, cap = p.cap > 0.f;
-  if (fast) return cap ? launch_k<D, G, true, true, WIN, ROPE, OT>(r, p) : launch_k<D, G, true, false, WIN, ROPE, OT>(r, p);
-  return cap ? launch_k<D, G, false, true, WIN, ROPE, OT>(r, p) : launch_k<D, G, false, false, WIN, ROPE, OT>(r, p);
+  if (fast) return cap ? launch_k<D, G, true, true, WIN, ROPE, MASK, OT>(r, p) : launch_k<D, G, true, false, WIN, ROPE, MASK, OT>(r, p);
+  return cap ? launch_k<D, G, false, true, WIN, ROPE, MASK, OT>(r, p) : launch_k<D, G, false, false, WIN, ROPE, MASK, OT>(r, p);
 }
 
-template <int D, bool WIN, bool ROPE, typename OT>
+template <int D, bool WIN, bool ROPE, bool MASK, typename OT>
 int launch_g(const RunArgs& r, const PrefillParams& p) {
   switch (r.G) {
-    case 1: return launch_t<D, 1, WIN, ROPE, OT>(r, p);
-    case 2: return launch_t<D, 2, WIN, ROPE, OT>(r, p);
-    case 4: return launch_t<D, 4, WIN, ROPE, OT>(r, p);
-    case 8: return launch_t<D, 8, WIN, ROPE, OT>(r, p);
+    case 1: return launch_t<D, 1, WIN, ROPE, MASK, OT>(r, p);
+    case 2: return launch_t<D, 2, WIN, ROPE, MASK, OT>(r, p);
+    case 4: return launch_t<D, 4, WIN, ROPE, MASK, OT>(r, p);
+    case 8: return launch_t<D, 8, WIN, ROPE, MASK, OT>(r, p);
   }
   return set_error(FI_ERR_UNSUPPORTED, "prefill: group size %d", r.G);
 }
 
-template <bool WIN, bool ROPE, typename OT>
+template <bool WIN, bool ROPE, bool MASK, typename OT>
 int launch_d(const RunArgs& r, const PrefillParams& p) {
-  if (r.D == 64) return launch_g<64, WIN, ROPE, OT>(r, p);
-  if (r.D == 128) return launch_g<128, WIN, ROPE, OT>(r, p);
+  if (r.D == 64) return launch_g<64, WIN, ROPE, MASK, OT>(r, p);
+  if (r.D == 128) return launch_g<128, WIN, ROPE, MASK, OT>(r, p);
   return set_error(FI_ERR_UNSUPPORTED, "prefill: head_dim %d", r.D);
 }
 
 // The kernels of one window / rotary mode, for the output type of the call.
-template <bool WIN, bool ROPE>
+template <bool WIN, bool ROPE, bool MASK = false>
 int launch_mode(const RunArgs& r, const PrefillParams& p) {
-  if (r.out_dtype == FI_BF16) return launch_d<WIN, ROPE, BF16>(r, p);
-  return launch_d<WIN, ROPE, F32>(r, p);
+  if (r.out_dtype == FI_BF16) return launch_d<WIN, ROPE, MASK, BF16>(r, p);
+  return launch_d<WIN, ROPE, MASK, F32>(r, p);
 }
 
 }  // namespace
 
-// defined in prefill_window.hip and prefill_rope.hip
+// defined in prefill_window.hip, prefill_rope.hip and prefill_mask.hip
 int launch_prefill_window(const RunArgs& r, const PrefillParams& p);
 int launch_prefill_rope(const RunArgs& r, const PrefillParams& p);
+int launch_prefill_mask(const RunArgs& r, const PrefillParams& p);
 
 }  // namespace fi

@@ -37,6 +37,12 @@ class DeviceBatch:
         self.kv_indptr = _dev_i32(b.kv_indptr)
         self.kv_indices = _dev_i32(b.kv_indices)
         self.last = _dev_i32(b.kv_last_page_len)
+        self.mask = self.mask_indptr = None
+        self.mask_bits = 0
+        if getattr(b, "tree_mask", None) is not None:
+            self.mask = torch.from_numpy(fi.tree_mask_words(b.tree_mask)).cuda()
+            self.mask_indptr = _dev_i32(b.mask_indptr)
+            self.mask_bits = int(b.mask_indptr[-1])
 
 
 def plan_for(b, workers_decode, workers_prefill=1, min_seg_pages=8, no_split=0, br_override=0,
@@ -64,7 +70,8 @@ def run(b, workers_decode=None, workers_prefill=None, min_seg_pages=8, no_split=
     lse = torch.full(tuple(b.q.shape[:2]), float("nan"), dtype=torch.float32, device="cuda") if with_lse else None
     ws = torch.empty(max(plan.float_ws_bytes // 4, 64), dtype=torch.float32, device="cuda")
     params = fi.make_params(b.dtype, out_dtype, b.num_qo_heads, Hk, b.head_dim, b.page_size,
-                            b.sm_scale, b.soft_cap)
+                            b.sm_scale, b.soft_cap, tree_mask=d.mask, mask_indptr=d.mask_indptr,
+                            mask_bits=d.mask_bits)
     if b.qo_indptr is None:
         fi.fi_batch_decode_paged(plan, plan_dev, params, d.q, d.pool, d.kv_indptr, d.kv_indices,
                                  d.last, o, lse, ws)
