@@ -696,9 +696,32 @@ void prefill_kernel(PrefillParams a) {
         step(n, cur, std::integral_constant<int, WIN ? 2 : 1>{});
       else step(n, cur, std::integral_constant<int, 0>{});
     };
-    for (int n = 0; n < ntiles; n += 2) {
-      step_any(n, std::false_type{});
-      if (n + 1 < ntiles) step_any(n + 1, std::true_type{});
+    // A wave whose 32 rows all lie past the tile's end (tiles of fewer than
+    // 128 rows) has nothing to compute: per tile it does only its share of
+    // the staging -- its quarter of the K loads and its V pieces -- and the
+    // barrier, so the busy waves of the tile and the other workgroup on the
+    // CU get its issue slots.  (The rotary kernels turn K in LDS with every
+    // thread and keep the full step.)
+    auto stage_only = [&](int n, auto cur) {
+      constexpr bool B1 = decltype(cur)::value;
+      dma_k(cx, n + 1, B1 ? k_lds0 : k_lds1, pk);
+      load_v(cx, n + 1, pv_ids);
+      pk = fetch_k(cx, n + 2);
+      pv_ids = fetch_v(cx, n + 2);
+      store_v(B1 ? v_lds0 : v_lds1);
+      FI_WAIT_VMCNT(0);
+      __syncthreads();
+    };
+    if (!ROPE && rb + kRowsPerWave * wave_u >= re) {
+      for (int n = 0; n < ntiles; n += 2) {
+        stage_only(n, std::false_type{});
+        if (n + 1 < ntiles) stage_only(n + 1, std::true_type{});
+      }
+    } else {
+      for (int n = 0; n < ntiles; n += 2) {
+        step_any(n, std::false_type{});
+        if (n + 1 < ntiles) step_any(n + 1, std::true_type{});
+      }
     }
 
 
