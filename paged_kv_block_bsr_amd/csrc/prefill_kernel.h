@@ -561,13 +561,14 @@ void prefill_kernel(PrefillParams a) {
         }
       }
     };
-    // the two words of a block's mask window (see prepare); the word index
-    // is clamped to the stream's last word, past which no bit is read
+    // the two words of a block's mask window (see prepare); word indices are
+    // clamped into [0, the stream's last word], so a malformed mask_indptr
+    // reads wrong bits but never outside the mask
     auto mask_window = [&](int n, int b) -> uint64_t {
       const int ub = t0 + n * kTileK + 32 * b + 4 * hh - causal_off;
       const int w0 = (mrow + max(ub, 0)) >> 5;
-      const uint32_t lo_w = a.mask[min(w0, a.mask_last_word)];
-      const uint32_t hi_w = a.mask[min(w0 + 1, a.mask_last_word)];
+      const uint32_t lo_w = a.mask[min(max(w0, 0), a.mask_last_word)];
+      const uint32_t hi_w = a.mask[min(max(w0 + 1, 0), a.mask_last_word)];
       return (uint64_t)lo_w | ((uint64_t)hi_w << 32);
     };
     // Online softmax of a prepared block, in two parts.  update_max: the
