@@ -226,3 +226,36 @@ def test_append_rejects_bad_arguments():
     assert L.fi_append_paged_kv(*args()) == -1                   # null pointers with tokens
     assert L.fi_append_paged_kv(*args(hk=1, d=4)) == -2          # 8-byte rows
     assert "token row" in fi.fi_last_error()
+
+
+def test_tree_mask_arguments_are_checked_without_a_gpu():
+    """Tree-mask checks happen on the host before any launch: mask_indptr and
+    a bit count in [1, 2^31), word alignment, no rotary embedding, a causal
+    plan without a window, and no cascade."""
+    torch = __import__("torch")
+    L = fi.lib()
+    kw = dict(page_size=16, num_qo_heads=8, num_kv_heads=2, head_dim=128, workers_decode=2,
+              workers_prefill=2)
+    plan = fi.fi_plan([0, 3], [0, 2], [3], causal=True, **kw)
+
+    def prefill(params, p=plan):
+        return L.fi_batch_prefill_paged(p.host_ptr(), 16, ctypes.byref(params), 16, 16, 10, 16, 16,
+                                        16, 16, 16, None, 16, 1 << 24, None)
+
+    mk = lambda **k: fi.make_params(torch.bfloat16, torch.bfloat16, 8, 2, 128, 16, **k)
+    assert prefill(mk(tree_mask=64, mask_indptr=None, mask_bits=9)) == fi.binding.FI_ERR_INVALID_ARG
+    assert prefill(mk(tree_mask=64, mask_indptr=64, mask_bits=0)) == fi.binding.FI_ERR_INVALID_ARG
+    assert prefill(mk(tree_mask=64, mask_indptr=64, mask_bits=1 << 31)) == fi.binding.FI_ERR_INVALID_ARG
+    assert prefill(mk(tree_mask=66, mask_indptr=64, mask_bits=9)) == fi.binding.FI_ERR_INVALID_ARG
+    assert "aligned" in fi.fi_last_error()
+    assert prefill(mk(tree_mask=64, mask_indptr=64, mask_bits=9, rope_theta=1e4)) == fi.binding.FI_ERR_UNSUPPORTED
+    nc = fi.fi_plan([0, 3], [0, 2], [3], causal=False, **kw)
+    assert prefill(mk(tree_mask=64, mask_indptr=64, mask_bits=9), nc) == fi.binding.FI_ERR_UNSUPPORTED
+    win = fi.fi_plan([0, 3], [0, 2], [3], causal=True, window_left=4, **kw)
+    assert prefill(mk(tree_mask=64, mask_indptr=64, mask_bits=9), win) == fi.binding.FI_ERR_UNSUPPORTED
+    p0 = fi.fi_plan([0, 1], [0, 2], [3], causal=False, **kw)
+    p1 = fi.fi_plan([0, 1], [0, 1], [5], causal=True, **kw)
+    rc = L.fi_cascade(p0.host_ptr(), 16, 16, 16, 16, 16, p1.host_ptr(), 16, 16, 16, 16, 16,
+                      ctypes.byref(mk(tree_mask=64, mask_indptr=64, mask_bits=1)), 16, 16, 10, 16,
+                      None, 16, 1 << 24, None)
+    assert rc == fi.binding.FI_ERR_UNSUPPORTED and "tree" in fi.fi_last_error()
