@@ -708,3 +708,35 @@ def test_tree_mask_rejects_non_causal_and_bad_offsets():
         ref.attention_of(b, causal=False)
     with pytest.raises(ref.OracleError):
         ref.attention_of(b, mask_indptr=np.array([0, 9, 12], np.int32))
+
+
+def test_tree_mask_matches_torch_sdpa_with_a_boolean_mask():
+    """The library routine as a second pin: torch's fp64 scaled-dot-product
+    attention over the request's gathered keys with the boolean mask built
+    from the parent array (prefix columns all true, draft columns true for
+    the row's own token and its ancestors)."""
+    import workloads as wl
+    qo, kv = [9, 4], [30, 4]
+    b, parents = _tree_batch(608, qo, kv, 4, D=16)
+    o, lse = ref.attention_of(b)
+    F = torch.nn.functional
+    qi = b.qo_indptr
+    for i in range(2):
+        K, V = _keys_of(b, i)
+        n, L = qo[i], K.shape[0]
+        m = torch.zeros(n, L, dtype=torch.bool)
+        m[:, :L - n] = True
+        for t in range(n):
+            u = t
+            while u >= 0:
+                m[t, L - n + u] = True
+                u = int(parents[i][u])
+        Q = b.q[qi[i]:qi[i] + n].double().permute(1, 0, 2)[None]                  # [1, Hq, n, D]
+        Kt = torch.from_numpy(K.astype(np.float64)).permute(1, 0, 2)[None].repeat_interleave(2, dim=1)
+        Vt = torch.from_numpy(V.astype(np.float64)).permute(1, 0, 2)[None].repeat_interleave(2, dim=1)
+        out = F.scaled_dot_product_attention(Q, Kt, Vt, attn_mask=m, scale=b.sm_scale)
+        np.testing.assert_allclose(o[qi[i]:qi[i] + n], out[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+        s = torch.einsum("bhtd,bhjd->bhtj", Q, Kt) * b.sm_scale
+        s = s.masked_fill(~m, -math.inf)
+        np.testing.assert_allclose(lse[qi[i]:qi[i] + n], torch.logsumexp(s, dim=-1)[0].T.numpy(),
+                                   rtol=0, atol=1e-12)
