@@ -124,7 +124,11 @@ def run_decode_bench(args):
                           workers_prefill=1, min_seg_pages=args.min_seg_pages,
                           out=pinned[j].numpy())
         info["plan"] = plan
-        plan_dev[j].copy_(pinned[j], non_blocking=True)  # whole buffer: no per-step slicing
+        # only the plan's own ints: a copy of a few KiB runs as a short blit
+        # on the stream, where the whole capacity buffer (> 16 KiB with many
+        # workers) went to the DMA engine and left a ~20 us gap per step
+        n = plan.ints
+        plan_dev[j][:n].copy_(pinned[j][:n], non_blocking=True)
         copied[j].record()
         if timed_idx in starts:
             starts[timed_idx].record()
@@ -361,15 +365,16 @@ ROPE_THETA = 500000.0  # rotary base of the Llama-3 family
 
 
 def rope_measurements(ps, steps):
-    """Fused rotary embedding on q and k: the decode workload (two worker
-    counts: the rotary decode kernel runs two waves per SIMD) and the prefill
-    slice of the mixed step.  Same algorithmic bytes and flops as without it."""
+    """Fused rotary embedding on q and k: the decode workload (the default
+    worker count and 8 per CU, as many as the rotary decode kernel's two waves
+    per SIMD hold) and the prefill slice of the mixed step.  Same algorithmic
+    bytes and flops as without it."""
     import workloads as wl
     import paged_kv_block_bsr_amd as fi
     db = wl.llama8b_decode()
     nb = decode_bytes(db)
     out = {"rope_theta": ROPE_THETA, "decode": {"workload": "llama8b_decode, rotary embedding"}}
-    for w in (fi.fi_default_workers(fi.FI_KIND_DECODE, NUM_CUS, db.num_kv_heads), 2 * NUM_CUS // db.num_kv_heads):
+    for w in (fi.fi_default_workers(fi.FI_KIND_DECODE, NUM_CUS, db.num_kv_heads), 8 * NUM_CUS // db.num_kv_heads):
         ms, _ = time_batch_call(db, steps, 3, workers_decode=w, rope_theta=ROPE_THETA)
         out["decode"][f"workers_{w}"] = {"us": round(ms * 1e3, 2), "gbs": round(nb / (ms * 1e-3) / 1e9, 1),
                                          "frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}

@@ -325,8 +325,9 @@ int fi_version(void) { return 100; }
 
 int fi_default_workers(int kind, int num_cus, int num_kv_heads) {
   if (num_cus < 1 || num_kv_heads < 1) return 1;
-  // decode: 3 workgroups of 4 waves per CU (3 waves per SIMD); prefill: 2 per CU
-  const int per_cu = kind == FI_KIND_PREFILL ? 2 : 3;
+  // decode: 6 one-wave workgroups per CU (1.5 waves per SIMD: every worker
+  // resident, none waiting for a slot); prefill: 2 workgroups of 4 waves per CU
+  const int per_cu = kind == FI_KIND_PREFILL ? 2 : 6;
   int w = per_cu * num_cus / num_kv_heads;
   return w < 1 ? 1 : w;
 }
