@@ -32,7 +32,7 @@ struct MergeParams {
 constexpr int kMergeRows = 16;  // packed rows per merge block (grid z covers a 128-row tile)
 
 // Block (task, g, z) merges rows 16 z .. 16 z + 15 of split row `task`.
-// Threads take (row, 4-dim chunk) units; when there are fewer units than
+// Threads take (row, 16-dim chunk) units; when there are fewer units than
 // threads, the slots are also divided among thread groups.  Each thread
 // folds its slots into a running (max, sum, weighted o) state as it reads
 // them -- lse and o of a slot are loaded together, so a block needs one
@@ -60,26 +60,33 @@ __global__ __launch_bounds__(kThreads) void merge_partials_kernel(MergeParams a)
   const int D = a.D, G = a.G;
   const int tid = threadIdx.x;
 
-  __shared__ f32x4_t red_acc[kThreads];
+  // A unit is one row's 16 consecutive dims (4 x 16-byte pieces): with few
+  // units per row, more thread groups share a row's slots, so a row split
+  // into hundreds of slots (one very long request) is folded by many groups
+  // in parallel rather than by one thread walking them all.
+  constexpr int NV = 4;  // 16-byte pieces per unit
+  __shared__ f32x4_t red_acc[kThreads][NV];
   __shared__ float red_m[kThreads], red_l[kThreads];
-  auto write_out = [&](int rr, int c, f32x4_t acc, float m, float l) {
+  auto write_out = [&](int rr, int c, f32x4_t (&acc)[NV], float m, float l) {
     const bool empty = m == neg_inf() || !(l > 0.f);
     const float inv = empty ? 0.f : 1.f / l;
-    acc *= inv;
     const int packed = rb + r0 + rr;
     const int64_t orow = (int64_t)(qbase + packed / G) * a.Hq + g * G + packed % G;
-    if (a.out_bf16) {
-      const uint32_t lo = pack_bf16x2(acc[0], acc[1]);
-      const uint32_t hi = pack_bf16x2(acc[2], acc[3]);
-      reinterpret_cast<uint32_t*>(a.o)[(orow * D + 4 * c) / 2] = lo;
-      reinterpret_cast<uint32_t*>(a.o)[(orow * D + 4 * c) / 2 + 1] = hi;
-    } else {
-      *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.o) + orow * D + 4 * c) = acc;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const f32x4_t x = acc[v] * inv;
+      const int64_t at = orow * D + 4 * (NV * c + v);
+      if (a.out_bf16) {
+        reinterpret_cast<uint32_t*>(a.o)[at / 2] = pack_bf16x2(x[0], x[1]);
+        reinterpret_cast<uint32_t*>(a.o)[at / 2 + 1] = pack_bf16x2(x[2], x[3]);
+      } else {
+        *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.o) + at) = x;
+      }
     }
     if (a.lse && c == 0) a.lse[orow] = empty ? neg_inf() : m + __logf(l);
   };
-  const int chunks = D / 4;
-  const int U = nr * chunks;  // (row, 4-dim chunk) units
+  const int chunks = D / (4 * NV);
+  const int U = nr * chunks;  // (row, 16-dim chunk) units
   int UP = 1;
   while (UP < U) UP <<= 1;
   const int ngroups = UP >= kThreads ? 1 : kThreads / UP;
@@ -87,24 +94,31 @@ __global__ __launch_bounds__(kThreads) void merge_partials_kernel(MergeParams a)
   for (int u = (UP >= kThreads ? tid : tid % UP); u < U; u += (UP >= kThreads ? kThreads : UP)) {
     const int rr = u / chunks, c = u % chunks;
     float m = neg_inf(), l = 0.f;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
+    f32x4_t acc[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) acc[v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
     for (int s = s0 + sg; s < s1; s += ngroups) {
       const int64_t pr = ((int64_t)s * a.Hk + g) * stride + r0 + rr;
       const float x = wl[pr];
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(wo + pr * D + 4 * c);
+      f32x4_t vv[NV];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) vv[v] = *reinterpret_cast<const f32x4_t*>(wo + pr * D + 4 * (NV * c + v));
       if (x > m) {  // a new running max: rescale what is there (exp(-inf) = 0 on the first slot)
         const float r = __expf(m - x);
-        acc *= r;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[v] *= r;
         l *= r;
         m = x;
       }
       const float w = x == neg_inf() ? 0.f : __expf(x - m);
-      acc += w * v;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) acc[v] += w * vv[v];
       l += w;
     }
     if (ngroups > 1) {
-      red_acc[tid] = acc;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) red_acc[tid][v] = acc[v];
       red_m[tid] = m;
       red_l[tid] = l;
       break;  // one unit per thread when the slots are split among groups
@@ -116,13 +130,16 @@ __global__ __launch_bounds__(kThreads) void merge_partials_kernel(MergeParams a)
     if (tid < U) {
       float M = red_m[tid];
       for (int k = 1; k < ngroups; ++k) M = fmaxf(M, red_m[tid + k * UP]);
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4_t acc[NV];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) acc[v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       float L = 0.f;
       if (M != neg_inf()) {
         for (int k = 0; k < ngroups; ++k) {
           const float mk = red_m[tid + k * UP];
           const float w = mk == neg_inf() ? 0.f : __expf(mk - M);
-          acc += w * red_acc[tid + k * UP];
+#pragma unroll
+          for (int v = 0; v < NV; ++v) acc[v] += w * red_acc[tid + k * UP][v];
           L += w * red_l[tid + k * UP];
         }
       }
