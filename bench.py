@@ -329,7 +329,9 @@ def secondary_measurements(args):
     del sv
     cb = wl.shared_prefix_cascade()
     ms_flat, _ = time_batch_call(cb.flat, args.side_steps, 3)
-    ms_casc = time_cascade(cb, args.side_steps, 3)
+    # level 1 holds only short suffixes (50-200 tokens): segments of 2 pages
+    # spread them over the workers (8-page segments leave most of them idle)
+    ms_casc = time_cascade(cb, args.side_steps, 3, min_seg1=2)
     out["cascade"] = {"workload": "shared_prefix_cascade (64 requests, 2048-token prefix, soft-cap 30)",
                       "cascade_us": round(ms_casc * 1e3, 2), "flat_us": round(ms_flat * 1e3, 2),
                       "speedup": round(ms_flat / ms_casc, 3)}
@@ -445,7 +447,7 @@ def prefill_only(args):
             "prefill_items": int(plan.info.prefill_items), "steps": args.side_steps}
 
 
-def time_cascade(cb, steps, warmup):
+def time_cascade(cb, steps, warmup, min_seg0=8, min_seg1=8):
     import torch
 
     import paged_kv_block_bsr_amd as fi
@@ -455,8 +457,10 @@ def time_cascade(cb, steps, warmup):
     kw = dict(page_size=l0.page_size, num_qo_heads=l0.num_qo_heads, num_kv_heads=Hk,
               head_dim=l0.head_dim, workers_decode=fi.fi_default_workers(fi.FI_KIND_DECODE, NUM_CUS, Hk),
               workers_prefill=fi.fi_default_workers(fi.FI_KIND_PREFILL, NUM_CUS, Hk))
-    p0 = fi.fi_plan(l0.qo_indptr, l0.kv_indptr, l0.kv_last_page_len, causal=False, **kw)
-    p1 = fi.fi_plan(None, l1.kv_indptr, l1.kv_last_page_len, causal=True, **kw)
+    p0 = fi.fi_plan(l0.qo_indptr, l0.kv_indptr, l0.kv_last_page_len, causal=False,
+                    min_seg_pages=min_seg0, **kw)
+    p1 = fi.fi_plan(None, l1.kv_indptr, l1.kv_last_page_len, causal=True, min_seg_pages=min_seg1,
+                    **kw)
     i32 = lambda a: torch.from_numpy(np.asarray(a, np.int32)).to(dev)
     q, pool = l0.q.to(dev), l0.kv_pool.to(dev)
     o = torch.empty_like(q)
