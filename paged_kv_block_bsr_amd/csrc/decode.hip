@@ -750,8 +750,36 @@ void decode_mfma_kernel(DecodeParams a) {
     }
 
     // wave totals (sum over the 4 lanes of a head: l, l ^ 16, l ^ 32, l ^ 48),
-    // then merge the four waves through LDS
+    // then merge the waves through LDS -- or, with one wave, write straight
+    // from the accumulator: lane l holds dims 16 b + 4 kq .. + 3 of head
+    // l % 16, and its head's max and sum
     l_part = head_sum(l_part);
+    if constexpr (kWaves == 1) {
+      if (hS < G) {
+        const bool empty = m_run == neg_inf();
+        const float inv = empty ? 0.f : 1.f / l_part;
+        const float lse2 = empty ? neg_inf() : m_run + fast_log2(l_part);
+        if (slot < 0) {
+          const int64_t orow = (int64_t)qrow * a.Hq + g * G + hS;
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const f32x4_t x = oacc[b] * inv;
+            const int64_t at = orow * D + 16 * b + 4 * kq;
+            if constexpr (OT::kBytes == 2)
+              *reinterpret_cast<u32x2_t*>(a.o + at * 2) = u32x2_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+            else
+              *reinterpret_cast<f32x4_t*>(a.o + at * 4) = x;
+          }
+          if (a.lse && kq == 0) a.lse[orow] = lse2 * kLn2;
+        } else {
+          const int64_t prow = ((int64_t)slot * Hk + g) * G + hS;
+#pragma unroll
+          for (int b = 0; b < NB; ++b) *reinterpret_cast<f32x4_t*>(ws_o + prow * D + 16 * b + 4 * kq) = oacc[b] * inv;
+          if (kq == 0) ws_lse[prow] = lse2 * kLn2;
+        }
+      }
+      continue;
+    }
     if (lane < G) {
       m_lds[wave][lane] = m_run;
       l_lds[wave][lane] = l_part;
