@@ -99,7 +99,7 @@ def run_decode_bench(args):
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
     cap_ints, ws_bytes = fi.fi_plan_bounds(B, B, Hq, Hk, D, wd, 1)
-    ws = torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device=dev)
+    ws = fi.workspace(ws_bytes, dev)
     pinned = [torch.empty(cap_ints, dtype=torch.int32, pin_memory=True) for _ in range(2)]
     plan_dev = [torch.empty(cap_ints, dtype=torch.int32, device=dev) for _ in range(2)]
     copied = [torch.cuda.Event() for _ in range(2)]
@@ -255,7 +255,7 @@ def time_batch_call(b, steps, warmup, workers_decode=0, workers_prefill=0, pool_
     q = b.q.to(dev)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
-    ws = torch.empty(plan.float_ws_bytes // 4 + 64, dtype=torch.float32, device=dev)
+    ws = fi.workspace(plan.float_ws_bytes, dev)
     mask = mask_ip = None
     if getattr(b, "tree_mask", None) is not None:
         mask = torch.from_numpy(fi.tree_mask_words(b.tree_mask)).to(dev)
@@ -465,7 +465,7 @@ def time_cascade(cb, steps, warmup, min_seg0=8, min_seg1=8):
     q, pool = l0.q.to(dev), l0.kv_pool.to(dev)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
-    ws = torch.empty(fi.fi_cascade_workspace_bytes(p0, p1) // 4 + 64, dtype=torch.float32, device=dev)
+    ws = fi.workspace(fi.fi_cascade_workspace_bytes(p0, p1), dev)
     params = fi.make_params(l0.dtype, l0.dtype, l0.num_qo_heads, Hk, l0.head_dim, l0.page_size,
                             l0.sm_scale, l0.soft_cap)
     a0 = (p0, p0.to_device(dev), i32(l0.qo_indptr), i32(l0.kv_indptr), i32(l0.kv_indices),

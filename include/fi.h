@@ -19,9 +19,10 @@
  *
  * Conventions for every call.
  *   - Pointers marked "host" are CPU memory; "device" are GPU memory.  The
- *     caller owns every buffer; the library allocates no device memory and
- *     never synchronises: run calls only enqueue work on `stream` (a
- *     hipStream_t passed as void*; NULL means the null stream).
+ *     caller owns every buffer; the library allocates no device memory.
+ *     Run calls never synchronise: they only enqueue work on `stream` (a
+ *     hipStream_t passed as void*; NULL means the null stream).  Only
+ *     fi_read_status waits.
  *   - The KV pool has shape [pool_pages, 2, page_size, num_kv_heads,
  *     head_dim] (axis 1: 0 = K, 1 = V); row-major, contiguous.
  *   - Request i owns pages kv_indices[kv_indptr[i] .. kv_indptr[i+1]) in
@@ -77,7 +78,9 @@ typedef enum fi_dtype { FI_F32 = 0, FI_BF16 = 1 } fi_dtype;
  *   head_dim          64 or 128
  *   causal            0 or 1 (binds requests with qo_len >= 2)
  *   workers_decode, workers_prefill: persistent workers per KV head of the
- *                     decode and prefill kernels (grid = workers x KV heads)
+ *                     decode and prefill kernels (grid = workers x KV heads);
+ *                     2 (W - 1) num_kv_heads <= 65536 for each (else
+ *                     FI_ERR_UNSUPPORTED: the workspace's ticket bank)
  *   min_seg_pages     >= 1, smallest segment of the page stream one worker owns
  *   br_override       0 (tile rows from the mean query length) or 16/32/64/128
  *   no_split          1: one item per row, no partial slots (unsplit reference)
@@ -149,9 +152,9 @@ int fi_plan_bounds(int32_t batch_size, int64_t total_qo, int32_t num_qo_heads,
  *              this plan gives it work (kernels without work exit at once),
  *              so a call captured into a HIP graph stays valid when replayed
  *              with any later plan of the same shapes and worker counts
- *              (serving-engine page, "How FlashInfer Works": load balancing
- *              that survives CUDA graphs).  0: kernels without work are not
- *              launched.
+ *              (paper page, "Load balancing that survives CUDA graphs":
+ *              persistent kernels with fixed grids replayed inside a
+ *              captured graph).  0: kernels without work are not launched.
  *   rope_theta > 0: fused rotary embedding of q and k inside the kernels
  *              (paper page: fused rotary embeddings among the attention
  *              variants of its opening paragraph; "Customizable attention":
@@ -203,6 +206,26 @@ typedef struct fi_attn_params {
 } fi_attn_params;
 
 /*
+ * The float workspace (float_ws) of the run calls.  Its first
+ * fi_plan_info.float_ws_bytes bytes (fi_cascade_workspace_bytes for the
+ * cascade) hold a control region -- a status word and the tickets that let
+ * the last worker of a split row merge its partial results -- then the
+ * partial results themselves.  The control region sits at the start and has
+ * a fixed size whatever the plan; it must be zero the first time a workspace
+ * is used (zero-fill it once when it is allocated).  Every run call leaves the
+ * tickets as it found them, so one workspace serves any number of later
+ * calls and plans, in stream order.  Calls that run at the same time must not
+ * share a workspace.
+ *
+ * Status word (word 0 of the workspace; of the cascade's workspace for both
+ * of its levels): bit flags the kernels OR in and never clear.
+ *   FI_STATUS_BAD_PAGE  a page id at or past pool_pages was read; the kernels
+ *                       read page 0 in its place (never outside the pool), so
+ *                       the rows that saw it hold wrong values.
+ */
+#define FI_STATUS_BAD_PAGE 1
+
+/*
  * Batch decode over the paged KV cache: one query token per request
  * (serving-engine page, "The Interface", batch_decode_with_paged_kv_cache;
  * GQA head group packing; FlashDecoding split of long requests merged by
@@ -215,7 +238,10 @@ typedef struct fi_attn_params {
  *               arrays the plan was built from (kv_indices ids < pool_pages)
  *   o           device [B, num_qo_heads, head_dim] (out_dtype)
  *   lse         device float [B, num_qo_heads], or NULL
- *   float_ws    device scratch of at least float_ws_bytes (fi_plan_info)
+ *   float_ws    device workspace of at least float_ws_bytes (fi_plan_info),
+ *               zero-filled when first used (see above)
+ *   pool_pages  >= 1 whenever some row of the plan sees a KV page; kv_pool
+ *               and kv_indices may be NULL only when none does
  * Launches the persistent decode kernel (grid workers_decode x num_kv_heads)
  * and the partial-merge kernel on `stream`.
  */
@@ -234,6 +260,13 @@ int fi_batch_decode_paged(const int32_t* plan_host, const int32_t* plan_dev,
  *   qo_indptr   device int32 [B+1], the array the plan was built from
  *   q, o        device [total_qo, num_qo_heads, head_dim]; lse [total_qo, num_qo_heads] or NULL
  * Other arguments as fi_batch_decode_paged.
+ * Numeric range of the prefill kernel (requests with two or more queries;
+ * also fi_cascade's level 0): V takes part in the P.V product as fp16, so
+ * bf16 values of V are exact for 2^-17 <= |v| <= 65504 and zero; smaller
+ * ones are rounded to fp16's subnormal step (2^-24, far below the output
+ * tolerance), and larger ones are clamped to +-65504.  Keep |V| <= 65504 on
+ * this path.  q and k are not narrowed (bf16 products, fp32 sums) unless the
+ * rotary embedding is on (see rope_theta).
  */
 int fi_batch_prefill_paged(const int32_t* plan_host, const int32_t* plan_dev,
                            const fi_attn_params* params, const void* q, const void* kv_pool,
@@ -286,12 +319,12 @@ int fi_cascade(const int32_t* plan0_host, const int32_t* plan0_dev, const int32_
 /* Float workspace fi_cascade needs for these two plans (bytes, or < 0 on error). */
 int64_t fi_cascade_workspace_bytes(const int32_t* plan0_host, const int32_t* plan1_host);
 
-/* Thread-local message of the last error of this thread ("" if none). */
 /*
- * Paged KV append: write a step's new K/V tokens into their pages
- * (serving-engine page, "Dynamic Problem Shapes": the append stage, adding
- * new tokens to the KV cache; "Page-Level Attention": a request's tokens
- * fill the pages of its page table in order, page_size tokens per page).
+ * Paged KV append: write a step's new K/V tokens into their pages (talk page,
+ * Background, "Dynamic Problem Shapes": the append stage, adding new tokens
+ * to the KV cache; serving-engine page, "Page-Level Attention": a request's
+ * tokens fill the pages of its page table in order, page_size tokens per
+ * page).
  * The index arrays describe each request's pages after the append: request
  * i holds kv_len_i = (pages_i - 1) * page_size + kv_last_page_len[i] tokens
  * (0 without pages), and its n_i = append_indptr[i+1] - append_indptr[i] new
@@ -305,9 +338,11 @@ int64_t fi_cascade_workspace_bytes(const int32_t* plan0_host, const int32_t* pla
  *                       head_dim] (dtype), written in place
  *   kv_indptr, kv_indices (kv_indices_len entries), kv_last_page_len:
  *                       device int32 arrays of the page table
- * On the device, a token whose position would be negative (more new tokens
- * than the request holds), whose page-table entry lies outside kv_indices,
- * or whose page id is not below pool_pages is not written.  Returns
+ * Library contract beyond the pages (which define no such input): on the
+ * device, a token whose position would be negative (more new tokens than
+ * the request holds), whose page-table entry lies outside kv_indices, or
+ * whose page id is not below pool_pages is not written, and nothing else of
+ * the pool changes.  Returns
  * FI_ERR_INVALID_ARG for negative sizes, null pointers with tokens to write,
  * or buffers that are not 16-byte aligned; FI_ERR_UNSUPPORTED for a dtype
  * other than FI_F32 / FI_BF16 or a token row (num_kv_heads * head_dim
@@ -320,6 +355,16 @@ int fi_append_paged_kv(const void* append_k, const void* append_v, fi_dtype dtyp
                        int32_t head_dim, const int32_t* kv_indptr, const int32_t* kv_indices,
                        int64_t kv_indices_len, const int32_t* kv_last_page_len, void* stream);
 
+/*
+ * Read the status word of a float workspace into *status (host int32), and
+ * reset it to 0 afterwards if `clear` is nonzero.  Unlike the run calls this
+ * one waits: it synchronises `stream`, so call it after the run calls whose
+ * status is wanted, with none in flight on another stream.  Errors:
+ * FI_ERR_INVALID_ARG (null pointer), FI_ERR_HIP.
+ */
+int fi_read_status(const void* float_ws, int32_t* status, int32_t clear, void* stream);
+
+/* Thread-local message of the last error of this thread ("" if none). */
 const char* fi_last_error(void);
 
 /* Library version, major * 10000 + minor * 100 + patch. */

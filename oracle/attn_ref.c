@@ -14,14 +14,15 @@
  *     the last page holds kv_last_page_len[i] valid tokens (index arrays named
  *     in "The Interface" code block);
  *   - exact attention softmax(s) V over the visible keys, with s = scale * q.k,
- *     an optional logits soft-cap transform s <- cap * tanh(s / cap) (the
- *     "logits transform such as soft-capping" of the JIT paragraph), GQA head
+ *     an optional logits soft-cap transform s <- cap * tanh(s / cap) (paper
+ *     page, "Customizable attention, compiled just in time": soft-capping is
+ *     one of its logits transforms), GQA head
  *     grouping (query head h reads KV head h / G, "Head Group Packing"), and the
  *     causal mask of batch prefill (causal=True in "The Interface");
  *   - the (output, log-sum-exp) state of each query row, the quantity that
  *     FlashDecoding partials and merge_state combine ("FlashDecoding: Parallel
- *     KV Split"; "merge partial results with the log-sum-exp composition" in
- *     the load-balancing paragraph).
+ *     KV Split"; paper page, "Load balancing that survives CUDA graphs": the
+ *     partial results are combined by log-sum-exp composition).
  *
  * Method: naive per-token page gather and a plain two-pass softmax (max, then
  * exp-sum), all in double precision.  No tiling, no online rescaling.
@@ -49,7 +50,8 @@
  *     mask).  rope_scale <= 0 means 1.
  *   - tree mask (paper page, opening paragraph: speculative decoding verifies
  *     trees of guesses; "Customizable attention": a variant is a mask; the
- *     token trees of speculative decoding on the serving-engine page): with a
+ *     token trees of speculative decoding on the talk page, Background and
+ *     "Block Sparse Matrix"): with a
  *     mask given, the qo_len query tokens of a request are its draft tokens,
  *     stored as its last qo_len keys (the bottom-right alignment of the
  *     causal mask), and bit t * qo_len + u of the request's bit block

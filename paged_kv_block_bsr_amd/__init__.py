@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     FI_F32,
     FI_KIND_DECODE,
     FI_KIND_PREFILL,
+    FI_STATUS_BAD_PAGE,
     FIError,
     Plan,
     decode_plan_buffer,
@@ -23,8 +24,10 @@ from .binding import (  # noqa: F401
     fi_merge_state,
     fi_plan,
     fi_plan_bounds,
+    fi_read_status,
     fi_version,
     lib,
     make_params,
     tree_mask_words,
+    workspace,
 )

@@ -39,7 +39,10 @@ H_STREAM0, H_STREAM1 = 12, 32
 
 EXPORTS = ["fi_plan", "fi_plan_bounds", "fi_batch_decode_paged", "fi_batch_prefill_paged",
            "fi_merge_state", "fi_cascade", "fi_cascade_workspace_bytes", "fi_append_paged_kv",
-           "fi_last_error", "fi_version", "fi_default_workers"]
+           "fi_read_status", "fi_last_error", "fi_version", "fi_default_workers"]
+
+# status word bits (fi_read_status)
+FI_STATUS_BAD_PAGE = 1
 
 
 class FIError(RuntimeError):
@@ -122,6 +125,7 @@ def lib():
         L.fi_append_paged_kv.argtypes = [vp, vp, ctypes.c_int, vp, ctypes.c_int32, ctypes.c_int64, vp,
                                          ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          vp, vp, ctypes.c_int64, vp, vp]
+        L.fi_read_status.argtypes = [vp, i32p, ctypes.c_int32, vp]
         L.fi_cascade_workspace_bytes.restype = ctypes.c_int64
         L.fi_last_error.restype = ctypes.c_char_p
         L.fi_default_workers.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
@@ -326,6 +330,22 @@ def fi_append_paged_kv(append_k, append_v, append_indptr, kv_pool, kv_indptr, kv
                                     _ptr(append_indptr), append_indptr.numel() - 1, n, _ptr(kv_pool),
                                     pages, page_size, hk, d, _ptr(kv_indptr), _ptr(kv_indices),
                                     kv_indices.numel(), _ptr(kv_last_page_len), _stream(stream)))
+
+
+def workspace(nbytes: int, device="cuda") -> "torch.Tensor":
+    """A float workspace of at least ``nbytes`` bytes, zero-filled: its control
+    region (status word and merge counters) must be zero when first used, and
+    the run calls leave it so."""
+    return torch.zeros(max(int(nbytes), 4) // 4 + 64, dtype=torch.float32, device=device)
+
+
+def fi_read_status(float_ws, clear: bool = False, stream=None) -> int:
+    """The status word of a workspace (``fi_read_status``): bit
+    ``FI_STATUS_BAD_PAGE`` is set once a run call has met a page id outside the
+    pool.  Synchronises ``stream``; ``clear`` resets the word afterwards."""
+    out = ctypes.c_int32()
+    _check(lib().fi_read_status(_ptr(float_ws), ctypes.byref(out), int(bool(clear)), _stream(stream)))
+    return int(out.value)
 
 
 def fi_last_error() -> str:

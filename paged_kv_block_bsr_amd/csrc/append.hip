@@ -1,7 +1,7 @@
 // append.hip -- paged KV append (gfx950): a step's new K/V tokens into the
-// slots their page table gives them (serving-engine page, "Dynamic Problem
-// Shapes": the append stage; "Page-Level Attention": tokens fill a request's
-// pages in order).
+// slots their page table gives them (talk page, Background, "Dynamic Problem
+// Shapes": the append stage; serving-engine page, "Page-Level Attention":
+// tokens fill a request's pages in order).
 //
 // One wave per token.  A token's K row (num_kv_heads x head_dim elements) is
 // contiguous in both the input and the pool, as is its V row, so the wave

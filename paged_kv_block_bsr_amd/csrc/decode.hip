@@ -48,6 +48,7 @@ struct DecodeParams {
   uint8_t* o;
   float* lse;
   float* ws;
+  int32_t* status;     // status word: kStatusBadPage when a page id is not below pool_pages
   int64_t pool_pages;
   int32_t Hq, Hk, P;
   int32_t page_shift;  // log2(P) when P is a power of two >= 16, else -1
@@ -145,6 +146,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams a) {
   const int vc = lane % NC;   // V lane: 16-byte piece of the row
   const int hS = lane & 15;
 
+  uint32_t bad_page = 0;  // a page id outside the pool was read (page 0 was used instead)
   const int it_begin = wip[worker];
   const int it_end = wip[worker + 1];
   for (int it = it_begin; it < it_end; ++it) {
@@ -191,7 +193,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams a) {
 
     auto page_of = [&](int tok) -> int64_t {
       int pg = a.kv_indices[kvb + (FAST ? (tok >> a.page_shift) : tok / P)];
-      return (uint32_t)pg < (uint64_t)a.pool_pages ? (int64_t)pg : 0;  // never read outside the pool
+      const bool ok = (uint32_t)pg < (uint64_t)a.pool_pages;
+      bad_page |= !ok;
+      return ok ? (int64_t)pg : 0;  // never read outside the pool
     };
     // Page ids of this wave's chunks, 64 at a time: lane j holds the page of
     // the wave's chunk 64 * batch + j, read back with readlane when its loads
@@ -393,13 +397,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams a) {
     }
     __syncthreads();
   }
+  report_status(a.status, bad_page, kStatusBadPage);
 }
 
 // ---------------------------------------------------------------------------
 // bf16 decode with page_size a power of two: P.V on the matrix cores.  Pages
 // of >= 16 tokens hold a whole chunk (one page id per chunk); with pages of
-// 1, 2, 4 or 8 tokens (SMALLP: the column-vector BSR of the serving-engine
-// page, "One format for every KV layout") a chunk spans several pages and
+// 1, 2, 4 or 8 tokens (SMALLP: the column-vector sparse matrix of the talk
+// page, Key Findings and "Block Sparse Matrix") a chunk spans several pages and
 // each lane looks up the page of its own token.
 //
 // Per wave and 16-token chunk: K goes global -> VGPRs as the A operand of
@@ -474,6 +479,7 @@ void decode_mfma_kernel(DecodeParams a) {
   // epilogue scratch of its own: the V ring is already loading the next item
   __shared__ __align__(16) float acc_lds[kWaves * G * D];
 
+  uint32_t bad_page = 0;  // a page id outside the pool was read (page 0 was used instead)
   const int it_begin = wip[worker];
   const int it_end = wip[worker + 1];
   // An item's record is loaded while the previous item runs, so only the
@@ -525,7 +531,9 @@ void decode_mfma_kernel(DecodeParams a) {
       // pid_vec is this lane's own page id (token tk).  K piece 4 p + kq and
       // V piece 4 k + kq of that token: V load k of lane l lands at stage
       // bytes k 1024 + 16 l, i.e. piece 4 k + l / 16 of token l % 16.
-      const int64_t page = (uint32_t)pid_vec < (uint64_t)a.pool_pages ? pid_vec : 0;  // never outside the pool
+      const bool ok = (uint32_t)pid_vec < (uint64_t)a.pool_pages;
+      bad_page |= !ok;
+      const int64_t page = ok ? pid_vec : 0;  // never outside the pool
       const int tok = cs + min(tk, x.t1 - 1 - cs);
       const uint8_t* kaddr = a.kv + (page * page_stride + (int64_t)(tok & (P - 1)) * tok_stride + (int64_t)g * D) * 2;
 #pragma unroll
@@ -539,7 +547,9 @@ void decode_mfma_kernel(DecodeParams a) {
       return;
     }
     const int pid = __builtin_amdgcn_readlane(pid_vec, kth & 63);
-    const int64_t page = (uint32_t)pid < (uint64_t)a.pool_pages ? pid : 0;  // never read outside the pool
+    const bool ok = (uint32_t)pid < (uint64_t)a.pool_pages;
+    bad_page |= !ok;
+    const int64_t page = ok ? pid : 0;  // never read outside the pool
     const int slot0 = cs & (P - 1);
     const int last = x.t1 - 1 - cs;  // last valid token of the chunk (may exceed 15)
     const uint8_t* pbase = a.kv + (page * page_stride + (int64_t)g * D) * 2;
@@ -819,6 +829,7 @@ void decode_mfma_kernel(DecodeParams a) {
     }
     __syncthreads();
   }
+  report_status(a.status, bad_page, kStatusBadPage);
 }
 
 template <int D, int G, typename OT, bool ROPE, bool SMALLP>
@@ -886,6 +897,7 @@ int launch_decode(const RunArgs& r) {
   p.o = static_cast<uint8_t*>(r.o);
   p.lse = r.lse;
   p.ws = r.ws;
+  p.status = r.status;
   p.pool_pages = r.pool_pages;
   p.Hq = r.Hq;
   p.Hk = r.Hk;

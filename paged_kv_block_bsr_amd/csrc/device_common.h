@@ -78,6 +78,14 @@ __device__ __forceinline__ u32x4_t load16(const void* p) {
 
 #define FI_LDS __attribute__((address_space(3)))
 
+// Sets `bits` in the status word when `bad` is nonzero in some lane of the
+// wave: the lowest such lane does one vector-memory atomic OR.
+__device__ __forceinline__ void report_status(int32_t* status, uint32_t bad, int32_t bits) {
+  const uint64_t m = __ballot(bad != 0);
+  if (m != 0 && (uint32_t)__lane_id() == (uint32_t)(__ffsll((unsigned long long)m) - 1))
+    __hip_atomic_fetch_or(status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ---- rotary embedding (rotate-half form: the pair (x[d], x[d + D/2]) turns
 // by pos / scale * theta^(-2d/D)).  The host supplies, per pair d, the turn
 // per position as a 32-bit fixed-point fraction of a revolution; the angle of

@@ -112,6 +112,7 @@ RunArgs base_args(const int32_t* plan_dev, const fi_attn_params* p, const void* 
   a.o = o;
   a.lse = lse;
   a.ws = static_cast<float*>(ws);
+  a.status = static_cast<int32_t*>(ws);  // word 0 of the workspace's control region
   a.Hq = p->num_qo_heads;
   a.Hk = p->num_kv_heads;
   a.D = p->head_dim;
@@ -156,26 +157,37 @@ int run_plan(RunArgs a, const int32_t* ph, bool with_prefill, bool graph_safe) {
   return FI_OK;
 }
 
+// A plan in which some row sees KV pages makes the kernels read kv_indices
+// and the pool: both must be there, and the pool must hold page 0, which
+// stands in for an out-of-pool id.
+int check_pages(const int32_t* ph, const void* kv_pool, int64_t pool_pages,
+                const int32_t* kv_indices, const char* who) {
+  if (pool_pages < 0) return set_error(FI_ERR_INVALID_ARG, "%s: pool_pages < 0", who);
+  if (ph[H_ANY_PAGES] && (pool_pages < 1 || !kv_pool || !kv_indices))
+    return set_error(FI_ERR_INVALID_ARG,
+                     "%s: the plan reads KV pages, so kv_pool, kv_indices and pool_pages >= 1 are needed", who);
+  return FI_OK;
+}
+
 int check_common(const int32_t* plan_host, const int32_t* plan_dev, const fi_attn_params* params,
                  const void* q, const void* kv_pool, int64_t pool_pages, const int32_t* kv_indptr,
                  const int32_t* kv_indices, const int32_t* kv_last_page_len, const void* o,
-                 const void* float_ws, int64_t float_ws_bytes, const char* who) {
+                 const void* float_ws, int64_t float_ws_bytes, const char* who,
+                 bool decode_ws_only = false) {
   int rc;
   if ((rc = check_params(params))) return rc;
   if ((rc = check_plan(plan_host, params, who))) return rc;
   const int B = plan_host[H_BATCH];
   if (!plan_dev) return set_error(FI_ERR_INVALID_ARG, "%s: null device plan", who);
-  if (pool_pages < 0) return set_error(FI_ERR_INVALID_ARG, "%s: pool_pages < 0", who);
   if (B > 0 && (!kv_indptr || !kv_last_page_len))
     return set_error(FI_ERR_INVALID_ARG, "%s: null index array", who);
   if (plan_host[H_TOTAL_QO] > 0 && (!q || !o))
     return set_error(FI_ERR_INVALID_ARG, "%s: null q or o", who);
-  if (plan_host[H_TOTAL_QO] > 0 && (!kv_pool || !kv_indices) && pool_pages > 0)
-    return set_error(FI_ERR_INVALID_ARG, "%s: null kv_pool or kv_indices", who);
+  if ((rc = check_pages(plan_host, kv_pool, pool_pages, kv_indices, who))) return rc;
   if (!aligned16(q) || !aligned16(kv_pool) || !aligned16(o))
     return set_error(FI_ERR_INVALID_ARG, "%s: q, kv_pool and o must be 16-byte aligned", who);
-  const int64_t need = (int64_t)plan_host[H_WS_FLOATS] * 4;
-  if (need > 0 && (!float_ws || float_ws_bytes < need))
+  const int64_t need = decode_ws_only ? decode_ws_bytes(plan_host) : (int64_t)plan_host[H_WS_FLOATS] * 4;
+  if (!float_ws || float_ws_bytes < need)
     return set_error(FI_ERR_WORKSPACE_TOO_SMALL, "%s: float workspace %lld bytes, needs %lld", who,
                      (long long)float_ws_bytes, (long long)need);
   if (!aligned16(float_ws)) return set_error(FI_ERR_INVALID_ARG, "%s: float_ws alignment", who);
@@ -183,6 +195,30 @@ int check_common(const int32_t* plan_host, const int32_t* plan_dev, const fi_att
 }
 
 }  // namespace
+
+int64_t decode_ws_bytes(const int32_t* ph) {
+  if (!ph || ph[H_MAGIC] != kPlanMagic) return -1;
+  const int32_t* sd = ph + H_STREAM0;
+  const int64_t lse_floats = ((int64_t)sd[S_SLOTCAP] * ph[H_HQ] + 63) / 64 * 64;
+  return ((int64_t)sd[S_WS_LSE] + lse_floats) * 4;
+}
+
+int decode_paged(const int32_t* plan_host, const int32_t* plan_dev, const fi_attn_params* params,
+                 const void* q, const void* kv_pool, int64_t pool_pages, const int32_t* kv_indptr,
+                 const int32_t* kv_indices, const int32_t* kv_last_page_len, void* o, float* lse,
+                 void* float_ws, int64_t float_ws_bytes, void* stream, bool decode_ws_only) {
+  int rc = check_common(plan_host, plan_dev, params, q, kv_pool, pool_pages, kv_indptr, kv_indices,
+                        kv_last_page_len, o, float_ws, float_ws_bytes, "fi_batch_decode_paged",
+                        decode_ws_only);
+  if (rc) return rc;
+  if (plan_host[H_STREAM1 + S_NROWS] != 0 || plan_host[H_TOTAL_QO] != plan_host[H_BATCH])
+    return set_error(FI_ERR_PLAN_MISMATCH,
+                     "fi_batch_decode_paged: plan has multi-query requests; use fi_batch_prefill_paged");
+  RunArgs a = base_args(plan_dev, params, q, kv_pool, pool_pages, nullptr, kv_indptr, kv_indices,
+                        kv_last_page_len, o, lse, float_ws, params->out_dtype, plan_host, stream);
+  return run_plan(a, plan_host, false, params->graph_safe != 0);
+}
+
 }  // namespace fi
 
 using namespace fi;
@@ -207,15 +243,8 @@ int fi_batch_decode_paged(const int32_t* plan_host, const int32_t* plan_dev,
                           const int32_t* kv_indices, const int32_t* kv_last_page_len, void* o,
                           float* lse, void* float_ws, int64_t float_ws_bytes, void* stream) {
   clear_error();
-  int rc = check_common(plan_host, plan_dev, params, q, kv_pool, pool_pages, kv_indptr, kv_indices,
-                        kv_last_page_len, o, float_ws, float_ws_bytes, "fi_batch_decode_paged");
-  if (rc) return rc;
-  if (plan_host[H_STREAM1 + S_NROWS] != 0 || plan_host[H_TOTAL_QO] != plan_host[H_BATCH])
-    return set_error(FI_ERR_PLAN_MISMATCH,
-                     "fi_batch_decode_paged: plan has multi-query requests; use fi_batch_prefill_paged");
-  RunArgs a = base_args(plan_dev, params, q, kv_pool, pool_pages, nullptr, kv_indptr, kv_indices,
-                        kv_last_page_len, o, lse, float_ws, params->out_dtype, plan_host, stream);
-  return run_plan(a, plan_host, false, params->graph_safe != 0);
+  return decode_paged(plan_host, plan_dev, params, q, kv_pool, pool_pages, kv_indptr, kv_indices,
+                      kv_last_page_len, o, lse, float_ws, float_ws_bytes, stream, false);
 }
 
 int fi_batch_prefill_paged(const int32_t* plan_host, const int32_t* plan_dev,
@@ -284,8 +313,15 @@ int fi_cascade(const int32_t* plan0_host, const int32_t* plan0_dev, const int32_
     return set_error(FI_ERR_UNSUPPORTED, "fi_cascade: plans with a sliding window are not supported");
   if (plan0_host[H_TOTAL_QO] != plan1_host[H_TOTAL_QO])
     return set_error(FI_ERR_PLAN_MISMATCH, "fi_cascade: levels cover different query rows");
-  if (plan0_host[H_BATCH] > 0 && !qo_indptr0)
-    return set_error(FI_ERR_INVALID_ARG, "fi_cascade: null level-0 qo_indptr");
+  if (!plan0_dev || !plan1_dev) return set_error(FI_ERR_INVALID_ARG, "fi_cascade: null device plan");
+  if (plan0_host[H_BATCH] > 0 && (!qo_indptr0 || !kv_indptr0 || !kv_last_page_len0))
+    return set_error(FI_ERR_INVALID_ARG, "fi_cascade: null level-0 index array");
+  // level 1 may be a decode-only plan (qo_indptr1 NULL: one query per request)
+  const bool multi1 = plan1_host[H_TOTAL_QO] != plan1_host[H_BATCH] || plan1_host[H_STREAM1 + S_NROWS] != 0;
+  if (plan1_host[H_BATCH] > 0 && (!kv_indptr1 || !kv_last_page_len1 || (multi1 && !qo_indptr1)))
+    return set_error(FI_ERR_INVALID_ARG, "fi_cascade: null level-1 index array");
+  if ((rc = check_pages(plan0_host, kv_pool, pool_pages, kv_indices0, "fi_cascade level 0"))) return rc;
+  if ((rc = check_pages(plan1_host, kv_pool, pool_pages, kv_indices1, "fi_cascade level 1"))) return rc;
   const int64_t need = fi_cascade_workspace_bytes(plan0_host, plan1_host);
   if (need < 0) return (int)need;
   if (!float_ws || float_ws_bytes < need)
@@ -294,9 +330,8 @@ int fi_cascade(const int32_t* plan0_host, const int32_t* plan0_dev, const int32_
   if (!aligned16(float_ws) || !aligned16(q) || !aligned16(kv_pool) || !aligned16(o))
     return set_error(FI_ERR_INVALID_ARG, "fi_cascade: 16-byte alignment");
   const int64_t total_qo = plan1_host[H_TOTAL_QO];
-  if (total_qo > 0 && (!q || !o || !kv_pool))
-    return set_error(FI_ERR_INVALID_ARG, "fi_cascade: null q, o or kv_pool");
-  if (pool_pages < 0) return set_error(FI_ERR_INVALID_ARG, "fi_cascade: pool_pages < 0");
+  if (total_qo > 0 && (!q || !o))
+    return set_error(FI_ERR_INVALID_ARG, "fi_cascade: null q or o");
   // workspace: level-0 partials | level-1 partials | state 0 (o, lse) | state 1 (o, lse)
   auto al = [](int64_t b) { return (b + 255) / 256 * 256; };
   uint8_t* base = static_cast<uint8_t*>(float_ws);
@@ -313,10 +348,24 @@ int fi_cascade(const int32_t* plan0_host, const int32_t* plan0_dev, const int32_
   if ((rc = run_plan(a0, plan0_host, true, params->graph_safe != 0))) return rc;
   RunArgs a1 = base_args(plan1_dev, params, q, kv_pool, pool_pages, qo_indptr1, kv_indptr1,
                          kv_indices1, kv_last_page_len1, o1, l1, ws1, FI_F32, plan1_host, stream);
+  a1.status = a0.status;  // one status word per cascade workspace: its first word
   if ((rc = run_plan(a1, plan1_host, true, params->graph_safe != 0))) return rc;
   float* lse_out = lse ? lse : l1;  // without a caller lse, merge it in place
   return launch_merge_state(o0, l0, o1, l1, o, lse_out, rows, params->head_dim, FI_F32,
                             params->out_dtype, stream);
+}
+
+int fi_read_status(const void* float_ws, int32_t* status, int32_t clear, void* stream) {
+  clear_error();
+  if (!float_ws || !status) return set_error(FI_ERR_INVALID_ARG, "fi_read_status: null pointer");
+  hipStream_t s = (hipStream_t)stream;
+  int32_t word = 0;
+  hipError_t e = hipMemcpyAsync(&word, float_ws, sizeof(word), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e == hipSuccess && clear && word != 0) e = hipMemsetAsync(const_cast<void*>(float_ws), 0, sizeof(word), s);
+  if (e != hipSuccess) return set_error(FI_ERR_HIP, "fi_read_status: %s", hipGetErrorString(e));
+  *status = word;
+  return FI_OK;
 }
 
 const char* fi_last_error(void) { return g_error; }

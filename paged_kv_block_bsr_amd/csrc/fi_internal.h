@@ -14,6 +14,17 @@ int set_error(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3
 void clear_error();
 
 int build_plan(const fi_plan_in* in, int32_t* buf, int64_t capacity, fi_plan_info* info);
+
+// The decode call with its workspace given (fi_api.cpp).  decode_ws_only:
+// float_ws_bytes need only cover the control region and the decode stream's
+// regions, the part a decode call touches.
+int decode_paged(const int32_t* plan_host, const int32_t* plan_dev, const fi_attn_params* params,
+                 const void* q, const void* kv_pool, int64_t pool_pages, const int32_t* kv_indptr,
+                 const int32_t* kv_indices, const int32_t* kv_last_page_len, void* o, float* lse,
+                 void* float_ws, int64_t float_ws_bytes, void* stream, bool decode_ws_only);
+// Bytes of the workspace a decode call of this plan touches (its control
+// region and decode regions), or < 0 if the plan is malformed.
+int64_t decode_ws_bytes(const int32_t* plan_host);
 int plan_bounds(int32_t B, int64_t total_qo, int32_t Hq, int32_t Hk, int32_t D, int32_t Wd,
                 int32_t Wp, int64_t* plan_ints, int64_t* ws_bytes);
 
@@ -31,6 +42,7 @@ struct RunArgs {
   void* o;                      // direct outputs
   float* lse;                   // may be NULL
   float* ws;                    // float workspace base
+  int32_t* status;              // status word (bit flags, OR-ed by the kernels)
   int32_t Hq, Hk, D, P, G;
   int32_t causal;
   int32_t window;               // sliding window (keys before the query's own); -1 = none

@@ -134,6 +134,8 @@ int validate(const fi_plan_in& in) {
     return set_error(FI_ERR_INVALID_ARG, "fi_plan: br_override must be 0, 16, 32, 64 or 128");
   if (in.no_split != 0 && in.no_split != 1) return set_error(FI_ERR_INVALID_ARG, "fi_plan: no_split");
   if (in.window_left < -1) return set_error(FI_ERR_INVALID_ARG, "fi_plan: window_left < -1");
+  if (2 * ((int64_t)std::max(in.workers_decode, in.workers_prefill) - 1) * in.num_kv_heads > kWsCounterInts)
+    return set_error(FI_ERR_UNSUPPORTED, "fi_plan: 2 (workers - 1) num_kv_heads exceeds %d", kWsCounterInts);
   if (B > 0 && (!in.kv_indptr || !in.kv_last_page_len))
     return set_error(FI_ERR_INVALID_ARG, "fi_plan: null index array");
   if (B == 0 && !in.kv_indptr) return set_error(FI_ERR_INVALID_ARG, "fi_plan: null kv_indptr");
@@ -160,17 +162,19 @@ int validate(const fi_plan_in& in) {
 }
 
 // Float workspace regions (float units, each padded to 64 floats = 256 B):
-// decode partial o, decode partial lse, prefill partial o, prefill partial lse.
+// the control region (status word, ticket counters; fixed place and size),
+// then decode partial o, decode partial lse, prefill partial o, prefill
+// partial lse.
 void ws_layout(int32_t Hq, int32_t Hk, int32_t D, int32_t Wd, int32_t Wp, int64_t off[4],
                int64_t* total) {
   int64_t cap_d = 2 * (int64_t)(Wd - 1), cap_p = 2 * (int64_t)(Wp - 1);
   int64_t sz[4] = {align64(cap_d * Hq * D), align64(cap_d * Hq),
                    align64(cap_p * Hk * kMaxTileRows * D), align64(cap_p * Hk * kMaxTileRows)};
-  off[0] = 0;
-  off[1] = sz[0];
-  off[2] = sz[0] + sz[1];
-  off[3] = sz[0] + sz[1] + sz[2];
-  *total = sz[0] + sz[1] + sz[2] + sz[3];
+  off[0] = kWsControlInts;
+  off[1] = off[0] + sz[0];
+  off[2] = off[1] + sz[1];
+  off[3] = off[2] + sz[2];
+  *total = off[3] + sz[3];
 }
 
 }  // namespace
@@ -179,6 +183,8 @@ int plan_bounds(int32_t B, int64_t total_qo, int32_t Hq, int32_t Hk, int32_t D, 
                 int32_t Wp, int64_t* plan_ints, int64_t* ws_bytes) {
   if (B < 0 || total_qo < 0 || Hq < 1 || Hk < 1 || Hq % Hk || D < 1 || Wd < 1 || Wp < 1)
     return set_error(FI_ERR_INVALID_ARG, "fi_plan_bounds: bad arguments");
+  if (2 * ((int64_t)std::max(Wd, Wp) - 1) * Hk > kWsCounterInts)
+    return set_error(FI_ERR_UNSUPPORTED, "fi_plan_bounds: 2 (workers - 1) num_kv_heads exceeds %d", kWsCounterInts);
   const int64_t G = Hq / Hk;
   const int64_t rows_d = B;
   const int64_t rows_p = ceil_div(total_qo * G, 16) + B;
@@ -288,6 +294,7 @@ int build_plan(const fi_plan_in* inp, int32_t* buf, int64_t capacity, fi_plan_in
     d[S_WS_O] = (int32_t)off[k == 0 ? 0 : 2];
     d[S_WS_LSE] = (int32_t)off[k == 0 ? 1 : 3];
     d[S_KIND] = k;
+    d[S_WS_CNT] = (int32_t)kWsCounterAt[k];
     d[S_OFF_ROWS] = (int32_t)pos;
     for (const Row& r : s.rows) {
       buf[pos++] = r.req;
@@ -335,6 +342,10 @@ int build_plan(const fi_plan_in* inp, int32_t* buf, int64_t capacity, fi_plan_in
   buf[H_GROUP] = G;
   buf[H_WS_FLOATS] = (int32_t)ws_total;
   buf[H_WINDOW] = in.window_left;
+  int32_t any_pages = 0;
+  for (auto& s : st)
+    for (const Row& r : s.rows) any_pages |= r.vis > 0;
+  buf[H_ANY_PAGES] = any_pages;
   if (info) {
     info->plan_ints = pos;
     info->float_ws_bytes = ws_total * 4;

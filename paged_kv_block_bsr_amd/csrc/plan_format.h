@@ -24,21 +24,35 @@
 // items are local to the request (the kernel adds kv_indptr[request]); a
 // row's items cover its pages [first, first + visible_pages).
 //
-// The float workspace holds, per stream, partial outputs [slot_cap][Hk][tile][D]
-// and partial lse [slot_cap][Hk][tile] (fp32, natural log) at the float offsets
-// recorded in the stream descriptor; tile = G for decode, 128 for prefill.
+// The float workspace starts with a control region whose place and size do
+// not depend on the plan: word 0 is the status word (bit flags the kernels OR
+// in, read and cleared by the host), then per stream kWsCounterInts int32
+// ticket counters of split rows (counter s0 * Hk + g of the split row whose
+// first slot is s0, KV head g).  Counters are zero at rest: every call leaves
+// them as it found them, so the region must be zero once, when the workspace
+// is first used.  After it, per stream, partial outputs [slot_cap][Hk][tile][D]
+// and partial lse [slot_cap][Hk][tile] (fp32, natural log) at the float
+// offsets recorded in the stream descriptor; tile = G for decode, 128 for
+// prefill.
 #pragma once
 #include <stdint.h>
 
 namespace fi {
 
 constexpr int32_t kPlanMagic = 0x31504946;  // "FIP1"
-constexpr int32_t kPlanVersion = 2;
+constexpr int32_t kPlanVersion = 3;
 constexpr int kHeaderInts = 64;
 constexpr int kMetaInts = 8;  // ints per item_meta record
 // item_meta fields
 enum : int { M_REQ = 0, M_KVB = 1, M_KVLEN = 2, M_QOBASE = 3, M_QOLEN = 4, M_RB = 5, M_RE = 6 };
 constexpr int kMaxTileRows = 128;
+// workspace control region (int32 words): status word, then two counter banks
+constexpr int kWsCtrlInts = 64;
+constexpr int kWsCounterInts = 65536;  // per stream: 2 (W - 1) Hk must fit
+constexpr int64_t kWsCounterAt[2] = {kWsCtrlInts, kWsCtrlInts + kWsCounterInts};
+constexpr int64_t kWsControlInts = kWsCtrlInts + 2 * (int64_t)kWsCounterInts;
+// status word bits
+constexpr int32_t kStatusBadPage = 1;  // a page id at or past pool_pages was read (and replaced by page 0)
 // A request of a windowed plan needs kv_len + qo_len below this, so that the
 // kernels' key bounds stay inside int32.
 constexpr int64_t kWindowMaxTokens = (int64_t)1 << 30;
@@ -59,7 +73,8 @@ enum : int {
   H_WS_FLOATS = 11,
   H_STREAM0 = 12,
   H_STREAM1 = 32,
-  H_WINDOW = 52,  // sliding window: keys a query sees before its own; -1 = none
+  H_WINDOW = 52,     // sliding window: keys a query sees before its own; -1 = none
+  H_ANY_PAGES = 53,  // 1 if some row has visible KV pages (the run calls then read kv_indices and the pool)
 };
 
 // stream descriptor words (relative to H_STREAM0 / H_STREAM1)
@@ -81,6 +96,7 @@ enum : int {
   S_WS_LSE = 14,
   S_KIND = 15,
   S_OFF_META = 16,
+  S_WS_CNT = 17,  // int32 offset in the float workspace of this stream's ticket counters
   kStreamDescInts = 20,
 };
 

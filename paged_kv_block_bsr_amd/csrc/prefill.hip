@@ -21,6 +21,7 @@ int launch_prefill(const RunArgs& r) {
   p.o = static_cast<uint8_t*>(r.o);
   p.lse = r.lse;
   p.ws = r.ws;
+  p.status = r.status;
   p.pool_pages = r.pool_pages;
   p.Hq = r.Hq;
   p.Hk = r.Hk;

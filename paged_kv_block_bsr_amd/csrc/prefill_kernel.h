@@ -38,7 +38,8 @@
 //     fp16's normal range (the conversion saturates at +-65504), and fp16
 //     keeps 11 bits of P where bf16 keeps 8.
 //   - with a tree mask (MASK, speculative decoding: paper page, opening
-//     paragraph, and the token trees of the serving-engine page), the
+//     paragraph; the token trees of the talk page, Background and "Block
+//     Sparse Matrix"), the
 //     request's draft tokens are its last qo_len keys; tiles that reach the
 //     draft take the masked step, where each lane tests the bits of its row
 //     (two 32-bit words per 32-key block, loaded before the step's K/V
@@ -62,6 +63,7 @@ struct PrefillParams {
   uint8_t* o;
   float* lse;
   float* ws;
+  int32_t* status;     // status word: kStatusBadPage when a page id is not below pool_pages
   int64_t pool_pages;
   int32_t Hq, Hk, P;
   int32_t causal;
@@ -274,8 +276,13 @@ void prefill_kernel(PrefillParams a) {
   auto clamp_key = [&](const Ctx& c, int key) { return key < c.t1 ? key : c.t1 - 1; };
   // page ids are loaded raw and checked where they are used, a tile
   // later, so the load is never waited for early; an id outside the pool
-  // reads page 0 instead
-  auto checked = [&](int pg) -> uint32_t { return (uint32_t)pg < pool_lim ? (uint32_t)pg : 0u; };
+  // reads page 0 instead, and is reported in the status word at the end
+  uint32_t bad_page = 0;
+  auto checked = [&](int pg) -> uint32_t {
+    const bool ok = (uint32_t)pg < pool_lim;
+    bad_page |= !ok;
+    return ok ? (uint32_t)pg : 0u;
+  };
   auto raw_page = [&](const Ctx& c, int key) -> int { return c.kvi[(uint32_t)page_idx(key)]; };
   // With power-of-two pages of >= 16 tokens (FAST) a wave's 16 K keys sit
   // in one page (tiles start on 16-key boundaries), whose id is then
@@ -782,6 +789,7 @@ void prefill_kernel(PrefillParams a) {
     }
     item = nxt;
   }
+  report_status(a.status, bad_page, kStatusBadPage);
 }
 
 template <int D, int G, bool FAST, bool CAP, bool WIN, bool ROPE, bool MASK, typename OT>

@@ -57,8 +57,9 @@ def plan_for(b, workers_decode, workers_prefill=1, min_seg_pages=8, no_split=0, 
 
 
 def run(b, workers_decode=None, workers_prefill=None, min_seg_pages=8, no_split=0,
-        out_dtype=None, br_override=0, dev=None, with_lse=True):
-    """Run decode (qo_indptr None) or prefill; returns (o float32 cpu, lse cpu)."""
+        out_dtype=None, br_override=0, dev=None, with_lse=True, ws=None):
+    """Run decode (qo_indptr None) or prefill; returns (o float32 cpu, lse cpu).
+    ``ws``: a workspace to use (else a fresh zero-filled one)."""
     Hk = b.num_kv_heads
     wd = workers_decode or fi.fi_default_workers(fi.FI_KIND_DECODE, NUM_CUS, Hk)
     wp = workers_prefill or fi.fi_default_workers(fi.FI_KIND_PREFILL, NUM_CUS, Hk)
@@ -68,7 +69,8 @@ def run(b, workers_decode=None, workers_prefill=None, min_seg_pages=8, no_split=
     out_dtype = out_dtype or b.dtype
     o = torch.full(tuple(b.q.shape), float("nan"), dtype=out_dtype, device="cuda")
     lse = torch.full(tuple(b.q.shape[:2]), float("nan"), dtype=torch.float32, device="cuda") if with_lse else None
-    ws = torch.empty(max(plan.float_ws_bytes // 4, 64), dtype=torch.float32, device="cuda")
+    if ws is None:
+        ws = fi.workspace(plan.float_ws_bytes)
     params = fi.make_params(b.dtype, out_dtype, b.num_qo_heads, Hk, b.head_dim, b.page_size,
                             b.sm_scale, b.soft_cap, tree_mask=d.mask, mask_indptr=d.mask_indptr,
                             mask_bits=d.mask_bits)
@@ -123,7 +125,7 @@ def run_cascade(cb, workers_decode=None, workers_prefill=None, min_seg_pages=8, 
     o = torch.full(tuple(l0.q.shape), float("nan"), dtype=out_dtype, device="cuda")
     lse = torch.full(tuple(l0.q.shape[:2]), float("nan"), dtype=torch.float32, device="cuda")
     nbytes = fi.fi_cascade_workspace_bytes(plan0, plan1)
-    ws = torch.empty(nbytes // 4 + 64, dtype=torch.float32, device="cuda")
+    ws = fi.workspace(nbytes)
     params = fi.make_params(l0.dtype, out_dtype, l0.num_qo_heads, Hk, l0.head_dim, l0.page_size,
                             l0.sm_scale, l0.soft_cap)
     fi.fi_cascade(plan0, plan0.to_device(), d0.qo_indptr, d0.kv_indptr, d0.kv_indices, d0.last,

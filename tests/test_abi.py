@@ -19,6 +19,21 @@ from oracle import plan_ref as pr
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
+def _gpu_visible() -> bool:
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+# Tests that hand the run calls made-up device addresses (16, 64, ...) to
+# check that the host validation rejects a call before any launch.  Where a
+# GPU is visible, a check that regressed would launch kernels on those
+# addresses, so these run only where none is.
+fake_addresses = pytest.mark.skipif(_gpu_visible(), reason="made-up device addresses: host-only test")
+
+
 def declared_functions():
     src = open(os.path.join(ROOT, "include", "fi.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
@@ -166,6 +181,7 @@ def test_fi_plan_capacity_and_bounds():
         assert p.ints <= ints and p.float_ws_bytes <= ws
 
 
+@fake_addresses
 def test_run_calls_reject_bad_arguments_without_a_gpu():
     """Argument and plan checks happen on the host before any launch."""
     plan = fi.fi_plan(None, [0, 2], [3], page_size=16, num_qo_heads=8, num_kv_heads=2,
@@ -185,6 +201,7 @@ def test_run_calls_reject_bad_arguments_without_a_gpu():
     assert rc == fi.binding.FI_ERR_PLAN_MISMATCH
 
 
+@fake_addresses
 def test_cascade_rejects_windowed_plans_without_a_gpu():
     torch = __import__("torch")
     kw = dict(page_size=16, num_qo_heads=8, num_kv_heads=2, head_dim=128, workers_decode=2,
@@ -197,6 +214,7 @@ def test_cascade_rejects_windowed_plans_without_a_gpu():
     assert rc == fi.binding.FI_ERR_UNSUPPORTED and "window" in fi.fi_last_error()
 
 
+@fake_addresses
 def test_rope_arguments_are_checked_without_a_gpu():
     torch = __import__("torch")
     plan = fi.fi_plan(None, [0, 2], [3], page_size=16, num_qo_heads=8, num_kv_heads=2,
@@ -228,6 +246,7 @@ def test_append_rejects_bad_arguments():
     assert "token row" in fi.fi_last_error()
 
 
+@fake_addresses
 def test_tree_mask_arguments_are_checked_without_a_gpu():
     """Tree-mask checks happen on the host before any launch: mask_indptr and
     a bit count in [1, 2^31), word alignment, no rotary embedding, a causal
@@ -259,3 +278,61 @@ def test_tree_mask_arguments_are_checked_without_a_gpu():
                       ctypes.byref(mk(tree_mask=64, mask_indptr=64, mask_bits=1)), 16, 16, 10, 16,
                       None, 16, 1 << 24, None)
     assert rc == fi.binding.FI_ERR_UNSUPPORTED and "tree" in fi.fi_last_error()
+
+
+@fake_addresses
+def test_run_calls_need_the_pool_and_page_table_when_the_plan_reads_pages():
+    """A plan in which some row sees a KV page makes the kernels read
+    kv_indices and the pool (and page 0, which stands in for an out-of-pool
+    id): pool_pages < 1 or a null pool / page table is refused on the host."""
+    torch = __import__("torch")
+    L = fi.lib()
+    plan = fi.fi_plan(None, [0, 2], [3], page_size=16, num_qo_heads=8, num_kv_heads=2,
+                      head_dim=128, causal=True, workers_decode=2)
+    assert plan.buf[53] == 1
+    params = fi.make_params(torch.bfloat16, torch.bfloat16, 8, 2, 128, 16)
+    big = 1 << 24
+
+    def decode(pool, pool_pages, kv_indices):
+        return L.fi_batch_decode_paged(plan.host_ptr(), 16, ctypes.byref(params), 16, pool, pool_pages,
+                                       16, kv_indices, 16, 16, None, 16, big, None)
+
+    for args in ((16, 0, 16), (None, 10, 16), (16, 10, None), (16, -1, 16)):
+        assert decode(*args) == fi.binding.FI_ERR_INVALID_ARG, args
+    assert "pool" in fi.fi_last_error()
+    # the workspace (control region included) is always needed
+    rc = L.fi_batch_decode_paged(plan.host_ptr(), 16, ctypes.byref(params), 16, 16, 10, 16, 16, 16, 16,
+                                 None, None, 0, None)
+    assert rc == fi.binding.FI_ERR_WORKSPACE_TOO_SMALL
+
+
+@fake_addresses
+def test_cascade_checks_both_levels_index_arrays():
+    torch = __import__("torch")
+    L = fi.lib()
+    kw = dict(page_size=16, num_qo_heads=8, num_kv_heads=2, head_dim=128, workers_decode=2,
+              workers_prefill=2)
+    p0 = fi.fi_plan([0, 3], [0, 2], [3], causal=False, **kw)
+    p1 = fi.fi_plan([0, 2, 3], [0, 1, 2], [5, 4], causal=True, **kw)  # request 0 has 2 queries
+    params = fi.make_params(torch.bfloat16, torch.bfloat16, 8, 2, 128, 16)
+    big = 1 << 26
+
+    def cascade(l0, l1, pool_pages=10, pool=16):
+        return L.fi_cascade(p0.host_ptr(), 16, *l0, p1.host_ptr(), 16, *l1, ctypes.byref(params), 16, pool,
+                            pool_pages, 16, None, 16, big, None)
+
+    good = (16, 16, 16, 16)
+    for k in range(4):
+        bad = list(good)
+        bad[k] = None
+        assert cascade(tuple(bad), good) == fi.binding.FI_ERR_INVALID_ARG, ("level 0", k)
+        assert cascade(good, tuple(bad)) == fi.binding.FI_ERR_INVALID_ARG, ("level 1", k)
+    assert cascade(good, good, pool_pages=0) == fi.binding.FI_ERR_INVALID_ARG
+    assert cascade(good, good, pool=None) == fi.binding.FI_ERR_INVALID_ARG
+
+
+def test_read_status_rejects_null_pointers():
+    L = fi.lib()
+    out = ctypes.c_int32()
+    assert L.fi_read_status(None, ctypes.byref(out), 0, None) == fi.binding.FI_ERR_INVALID_ARG
+    assert L.fi_read_status(16, None, 0, None) == fi.binding.FI_ERR_INVALID_ARG

@@ -7,12 +7,14 @@
   the pages in order"), and nothing outside those slots changes;
 - appending in two steps (the page table growing in between) equals
   appending once, across page boundaries;
-- tokens beyond what a request holds are not written.
+- a new token with no place (the request does not hold it, or its page id
+  is outside the pool) is refused: the pages define no such input.
 """
 import json
 import os
 
 import numpy as np
+import pytest
 
 from oracle import append_ref as ap
 
@@ -101,13 +103,17 @@ def test_two_appends_equal_one():
     assert np.array_equal(step2, once)
 
 
-def test_more_new_tokens_than_the_request_holds():
+def test_tokens_without_a_place_are_refused():
+    """The pages define where a new token goes only when the request holds it
+    and its page-table entry names a page of the pool; the oracle raises on
+    anything else rather than pick a behaviour."""
     P = 4
     kv_indptr, kv_indices, last = _indptr([1]), np.array([2], np.int32), np.array([3], np.int32)
     k = np.arange(5, dtype=np.float64).reshape(5, 1, 1) + 1.0
     pool = np.zeros((4, 2, P, 1, 1))
-    out = ap.append(pool, k, k, np.array([0, 5], np.int32), kv_indptr, kv_indices, last, P)
-    # the request holds 3 tokens: only the last three new ones land, in slots 0..2
-    assert np.array_equal(out[2, 0, :3, 0, 0], [3.0, 4.0, 5.0])
-    out[2, :, :3] = 0.0
-    assert not out.any()
+    with pytest.raises(ap.Unplaceable):   # 5 new tokens, 3 held
+        ap.append(pool, k, k, np.array([0, 5], np.int32), kv_indptr, kv_indices, last, P)
+    with pytest.raises(ap.Unplaceable):   # a page id outside the pool
+        ap.append(pool, k[:2], k[:2], np.array([0, 2], np.int32), kv_indptr, np.array([9], np.int32), last, P)
+    out = ap.append(pool, k[:3], k[:3], np.array([0, 3], np.int32), kv_indptr, kv_indices, last, P)
+    assert np.array_equal(out[2, 0, :3, 0, 0], [1.0, 2.0, 3.0])

@@ -62,14 +62,33 @@ def test_append_sweep(dtype, D, Hk, P):
     _check(*_case(rng, P, Hk, D, dtype, kv_lens, new), f"sweep D={D} Hk={Hk} P={P}")
 
 
-def test_append_skips_what_it_cannot_place():
+def test_append_contract_for_tokens_without_a_place():
+    """Library contract (the pages define no such input): a new token that
+    the request does not hold, or whose page id lies outside the pool, is not
+    written and nothing else changes.  Expected pool: the oracle on the same
+    batch made placeable -- request 0 keeps only the new tokens it holds (the
+    last 5 of 9, whose positions do not change), and the two bad page-table
+    entries name a scratch page added past the pool, dropped afterwards."""
     rng = np.random.default_rng(8201)
     P = 16
     kv_lens = [5, 40, 33]
     new = [9, 3, 4]                          # request 0: 9 new tokens but only 5 held
     pool, k, v, a_ip, kv_ip, kv_idx, last = _case(rng, P, 2, 64, torch.bfloat16, kv_lens, new,
                                                   bad_pages=[(3, 10 ** 6), (5, -7)])
-    _check(pool, k, v, a_ip, kv_ip, kv_idx, last, "with unplaceable tokens")
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()
+    pool_d = pool.cuda()
+    note("append contract: 4 tokens past the request's start, 2 out-of-pool page ids")
+    fi.fi_append_paged_kv(k.cuda(), v.cuda(), i32(a_ip), pool_d, i32(kv_ip), i32(kv_idx), i32(last))
+    torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int16).numpy()
+    n_pages = pool.shape[0]
+    ext = np.concatenate([bits(pool), np.zeros((1,) + tuple(pool.shape[1:]), np.int16)])
+    idx = kv_idx.copy()
+    idx[3] = idx[5] = n_pages                # the scratch page
+    keep = np.r_[4:int(a_ip[-1])]            # drop request 0's first 4 new tokens
+    want = ap.append(ext, bits(k)[keep], bits(v)[keep], a_ip - np.array([0, 4, 4, 4], np.int32),
+                     kv_ip, idx, last, P)[:n_pages]
+    assert np.array_equal(bits(pool_d.cpu()), want), "append contract: pool differs"
 
 
 def test_append_mixed_step_new_tokens_full_size():

@@ -43,6 +43,31 @@ def test_mixed_ragged_step_sampled():
     assert_close(og, lg, o_ref, l_ref, "mixed_ragged_step")
 
 
+def test_mixed_ragged_step_full():
+    """Every (token, head) row of the mixed step -- 16 causal prefills and 48
+    decodes in one call -- against the oracle."""
+    b = wl.mixed_ragged_step(nan_poison=True)
+    note("mixed_ragged_step gpu, default workers")
+    o, lse, plan = run(b)
+    assert plan.info.prefill_rows > 0 and plan.info.decode_rows == 48
+    note(f"mixed_ragged_step oracle on all {b.total_qo * b.num_qo_heads} rows")
+    o_ref, l_ref = ref.attention_of(b)
+    assert_close(o, lse, o_ref, l_ref, "mixed_ragged_step full")
+
+
+def test_mixed_ragged_step_page_size_1_full():
+    """The mixed step stored one token per page (the column-vector layout),
+    every row against the oracle."""
+    m = wl.mixed_ragged_step()
+    b = wl.make_batch(1004, m.qo_lens, m.kv_lens, page_size=1, nan_poison=True)
+    note("mixed step P=1 gpu")
+    o, lse, plan = run(b)
+    assert plan.info.prefill_rows > 0 and plan.info.decode_rows == 48
+    note(f"mixed step P=1 oracle on all {b.total_qo * b.num_qo_heads} rows")
+    o_ref, l_ref = ref.attention_of(b)
+    assert_close(o, lse, o_ref, l_ref, "mixed P=1 full")
+
+
 def test_mixed_medium_full():
     qo = [64, 1, 130, 7, 1, 300, 2, 1]
     kv = [64 + 500, 900, 130, 7 + 33, 17, 300 + 1200, 2, 3000]
@@ -98,20 +123,6 @@ def test_prefill_page_sizes(P):
         note(f"prefill page size P={P} Wp={wp}")
         o, lse, _ = run(b, workers_decode=3, workers_prefill=wp, min_seg_pages=ms, dev=dev)
         assert_close(o, lse, o_ref, l_ref, f"prefill P={P} Wp={wp}")
-
-
-def test_mixed_ragged_step_page_size_1_sampled():
-    """The mixed step stored one token per page, sampled rows at full size."""
-    m = wl.mixed_ragged_step()
-    b = wl.make_batch(1004, m.qo_lens, m.kv_lens, page_size=1, nan_poison=True)
-    note("mixed step P=1 gpu")
-    o, lse, plan = run(b)
-    assert plan.info.prefill_rows > 0 and plan.info.decode_rows == 48
-    rows = _rows_for(b)
-    note(f"mixed step P=1 oracle on {len(rows)} sampled rows")
-    o_ref, l_ref = ref.attention_rows_of(b, rows)
-    og, lg = _gather(o, lse, b, rows)
-    assert_close(og, lg, o_ref, l_ref, "mixed P=1 sampled")
 
 
 def test_prefill_non_causal_empty_cache_and_f32_out():

@@ -33,7 +33,7 @@ def run_rope(b, theta, scale, workers_decode=None, workers_prefill=None, min_seg
     d = dev or DeviceBatch(b)
     o = torch.full(tuple(b.q.shape), float("nan"), dtype=b.dtype, device="cuda")
     lse = torch.full(tuple(b.q.shape[:2]), float("nan"), dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(plan.float_ws_bytes // 4, 64), dtype=torch.float32, device="cuda")
+    ws = fi.workspace(plan.float_ws_bytes)
     params = fi.make_params(b.dtype, b.dtype, b.num_qo_heads, Hk, b.head_dim, b.page_size, b.sm_scale,
                             b.soft_cap, rope_theta=theta, rope_scale=scale)
     if b.qo_indptr is None:
@@ -106,6 +106,16 @@ def test_rope_long_request_positions():
     o, lse, _ = run_rope(b, 500000.0, 1.0, workers_decode=64, min_seg_pages=1)
     o_ref, l_ref = ref.attention_of(b, rope_theta=500000.0)
     assert_close(o, lse, o_ref, l_ref, "rope long request")
+
+
+def test_rope_mixed_ragged_step_full():
+    b = wl.mixed_ragged_step(nan_poison=True)
+    note("mixed_ragged_step, rope theta 10000, default workers")
+    o, lse, plan = run_rope(b, 10000.0, 1.0)
+    assert plan.info.prefill_rows > 0 and plan.info.decode_rows == 48
+    note(f"mixed_ragged_step rope oracle on all {b.total_qo * b.num_qo_heads} rows")
+    o_ref, l_ref = ref.attention_of(b, rope_theta=10000.0)
+    assert_close(o, lse, o_ref, l_ref, "mixed rope full")
 
 
 def test_rope_mixed_ragged_step_sampled():

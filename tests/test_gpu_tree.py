@@ -85,7 +85,7 @@ def test_tree_mask_errors():
         plan = fi.fi_plan(b.qo_indptr, b.kv_indptr, b.kv_last_page_len, page_size=16,
                           num_qo_heads=8, num_kv_heads=2, head_dim=128, causal=causal,
                           workers_decode=2, workers_prefill=2, window_left=window)
-        ws = torch.empty(max(plan.float_ws_bytes // 4, 64), dtype=torch.float32, device="cuda")
+        ws = fi.workspace(plan.float_ws_bytes)
         params = fi.make_params(b.dtype, b.dtype, 8, 2, 128, 16, b.sm_scale, 0.0, tree_mask=d.mask,
                                 mask_indptr=d.mask_indptr, mask_bits=d.mask_bits)
         note(f"tree mask rejected: causal={causal} window={window}")

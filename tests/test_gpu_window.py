@@ -97,6 +97,17 @@ def test_window_llama8b_decode_full():
     assert_close(o, lse, o_ref, l_ref, "llama8b decode window 1023")
 
 
+def test_window_mixed_ragged_step_full():
+    b = wl.mixed_ragged_step(nan_poison=True)
+    b.window_left = 1023
+    note("mixed_ragged_step, window 1023, default workers")
+    o, lse, plan = run(b)
+    assert plan.info.prefill_rows > 0 and plan.info.decode_rows == 48
+    note(f"mixed_ragged_step window oracle on all {b.total_qo * b.num_qo_heads} rows")
+    o_ref, l_ref = ref.attention_of(b)
+    assert_close(o, lse, o_ref, l_ref, "mixed_ragged_step window 1023 full")
+
+
 def test_window_mixed_ragged_step_sampled():
     b = wl.mixed_ragged_step(nan_poison=True)
     b.window_left = 1023

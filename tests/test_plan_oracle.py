@@ -329,3 +329,21 @@ def test_window_zero_decode_rows_keep_only_the_last_page():
     for (r, pb, pe, slot) in st["items"]:
         n = int(npg[r])
         assert (pb, pe) == ((n - 1, n) if n else (0, 0))
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_any_pages_word_marks_plans_whose_rows_see_pages(seed):
+    """Header word 53 is 1 exactly when some request with queries has KV
+    tokens: such a row sees at least one page (a causal prefill row has
+    qo_len <= kv_len, so it sees its own key)."""
+    rng = np.random.default_rng(4400 + seed)
+    B = int(rng.integers(0, 6))
+    qo = rng.integers(0, 4, B) * rng.integers(0, 2, B)
+    kv = np.where((rng.random(B) < 0.5) & (qo < 2), 0, qo + rng.integers(0, 40, B))
+    npg = -(-kv // 16)
+    last = np.where(npg > 0, kv - (npg - 1) * 16, 0)
+    code, res = pr.plan(np.concatenate([[0], np.cumsum(qo)]), np.concatenate([[0], np.cumsum(npg)]), last,
+                        page_size=16, num_qo_heads=8, num_kv_heads=2, head_dim=64, causal=True,
+                        workers_decode=3, workers_prefill=2, window_left=int(rng.integers(-1, 20)))
+    assert code == pr.FI_OK
+    assert res["buf"][pr.ANY_PAGES_AT] == int(bool(np.any((qo >= 1) & (kv > 0))))
