@@ -356,11 +356,34 @@ int fi_append_paged_kv(const void* append_k, const void* append_v, fi_dtype dtyp
                        int64_t kv_indices_len, const int32_t* kv_last_page_len, void* stream);
 
 /*
+ * Batch decode that allocates nothing, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  As fi_batch_decode_paged, except that
+ * the float workspace is a static device array of the library, one per GPU,
+ * FI_NOALLOC_SCRATCH_BYTES long, held from load to process end.  A plan whose
+ * decode stream needs more (its control region plus 2 (workers_decode - 1)
+ * partial slots of num_qo_heads x head_dim floats and their lse) is refused
+ * with FI_ERR_WORKSPACE_TOO_SMALL before anything runs.  Every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU race, so keep them
+ * in one stream order.  Its status word is read with fi_read_status(NULL,
+ * ...) on the same device.  Never calls hipMalloc, hipFree or an allocating
+ * routine.
+ */
+#define FI_NOALLOC_SCRATCH_BYTES (16 << 20)
+int fi_batch_decode_paged_noalloc(const int32_t* plan_host, const int32_t* plan_dev,
+                                  const fi_attn_params* params, const void* q,
+                                  const void* kv_pool, int64_t pool_pages,
+                                  const int32_t* kv_indptr, const int32_t* kv_indices,
+                                  const int32_t* kv_last_page_len, void* o, float* lse,
+                                  void* stream);
+
+/*
  * Read the status word of a float workspace into *status (host int32), and
  * reset it to 0 afterwards if `clear` is nonzero.  Unlike the run calls this
  * one waits: it synchronises `stream`, so call it after the run calls whose
- * status is wanted, with none in flight on another stream.  Errors:
- * FI_ERR_INVALID_ARG (null pointer), FI_ERR_HIP.
+ * status is wanted, with none in flight on another stream.  float_ws NULL
+ * reads the static scratch of fi_batch_decode_paged_noalloc on the current
+ * device.  Errors: FI_ERR_INVALID_ARG (null status), FI_ERR_HIP.
  */
 int fi_read_status(const void* float_ws, int32_t* status, int32_t clear, void* stream);
 

@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     decode_plan_buffer,
     fi_append_paged_kv,
     fi_batch_decode_paged,
+    fi_batch_decode_paged_noalloc,
     fi_batch_prefill_paged,
     fi_cascade,
     fi_cascade_workspace_bytes,

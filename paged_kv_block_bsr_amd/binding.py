@@ -39,7 +39,8 @@ H_STREAM0, H_STREAM1 = 12, 32
 
 EXPORTS = ["fi_plan", "fi_plan_bounds", "fi_batch_decode_paged", "fi_batch_prefill_paged",
            "fi_merge_state", "fi_cascade", "fi_cascade_workspace_bytes", "fi_append_paged_kv",
-           "fi_read_status", "fi_last_error", "fi_version", "fi_default_workers"]
+           "fi_read_status", "fi_last_error", "fi_version", "fi_default_workers",
+           "fi_batch_decode_paged_noalloc"]
 
 # status word bits (fi_read_status)
 FI_STATUS_BAD_PAGE = 1
@@ -126,6 +127,8 @@ def lib():
                                          ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          vp, vp, ctypes.c_int64, vp, vp]
         L.fi_read_status.argtypes = [vp, i32p, ctypes.c_int32, vp]
+        L.fi_batch_decode_paged_noalloc.argtypes = [vp, vp, ctypes.POINTER(fi_attn_params), vp, vp,
+                                                    ctypes.c_int64, vp, vp, vp, vp, vp, vp]
         L.fi_cascade_workspace_bytes.restype = ctypes.c_int64
         L.fi_last_error.restype = ctypes.c_char_p
         L.fi_default_workers.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
@@ -279,6 +282,17 @@ def fi_batch_decode_paged(plan: Plan, plan_dev, params: fi_attn_params, q, kv_po
         _ptr(lse), _ptr(float_ws), float_ws.numel() * float_ws.element_size(), _stream(stream)))
 
 
+def fi_batch_decode_paged_noalloc(plan: Plan, plan_dev, params: fi_attn_params, q, kv_pool,
+                                  kv_indptr, kv_indices, kv_last_page_len, o, lse, stream=None):
+    """Batch decode with the library's static scratch as its workspace
+    (``fi_batch_decode_paged_noalloc``): no workspace argument, nothing
+    allocated."""
+    _check(lib().fi_batch_decode_paged_noalloc(
+        plan.host_ptr(), _ptr(plan_dev), ctypes.byref(params), _ptr(q), _ptr(kv_pool),
+        kv_pool.shape[0], _ptr(kv_indptr), _ptr(kv_indices), _ptr(kv_last_page_len), _ptr(o),
+        _ptr(lse), _stream(stream)))
+
+
 def fi_batch_prefill_paged(plan: Plan, plan_dev, params: fi_attn_params, q, kv_pool, qo_indptr,
                            kv_indptr, kv_indices, kv_last_page_len, o, lse, float_ws,
                            stream=None):
@@ -340,11 +354,13 @@ def workspace(nbytes: int, device="cuda") -> "torch.Tensor":
 
 
 def fi_read_status(float_ws, clear: bool = False, stream=None) -> int:
-    """The status word of a workspace (``fi_read_status``): bit
+    """The status word of a workspace (``fi_read_status``; None: the static
+    scratch of the no-alloc decode on the current device): bit
     ``FI_STATUS_BAD_PAGE`` is set once a run call has met a page id outside the
     pool.  Synchronises ``stream``; ``clear`` resets the word afterwards."""
     out = ctypes.c_int32()
-    _check(lib().fi_read_status(_ptr(float_ws), ctypes.byref(out), int(bool(clear)), _stream(stream)))
+    ws = None if float_ws is None else _ptr(float_ws)
+    _check(lib().fi_read_status(ws, ctypes.byref(out), int(bool(clear)), _stream(stream)))
     return int(out.value)
 
 

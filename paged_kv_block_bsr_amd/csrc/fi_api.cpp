@@ -357,7 +357,8 @@ int fi_cascade(const int32_t* plan0_host, const int32_t* plan0_dev, const int32_
 
 int fi_read_status(const void* float_ws, int32_t* status, int32_t clear, void* stream) {
   clear_error();
-  if (!float_ws || !status) return set_error(FI_ERR_INVALID_ARG, "fi_read_status: null pointer");
+  if (!status) return set_error(FI_ERR_INVALID_ARG, "fi_read_status: null status pointer");
+  if (!float_ws && !(float_ws = noalloc_scratch())) return FI_ERR_HIP;
   hipStream_t s = (hipStream_t)stream;
   int32_t word = 0;
   hipError_t e = hipMemcpyAsync(&word, float_ws, sizeof(word), hipMemcpyDeviceToHost, s);

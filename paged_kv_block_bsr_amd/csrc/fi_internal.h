@@ -25,6 +25,9 @@ int decode_paged(const int32_t* plan_host, const int32_t* plan_dev, const fi_att
 // Bytes of the workspace a decode call of this plan touches (its control
 // region and decode regions), or < 0 if the plan is malformed.
 int64_t decode_ws_bytes(const int32_t* plan_host);
+// The static scratch of fi_batch_decode_paged_noalloc on the current device
+// (its device address, looked up once per device), or NULL with the error set.
+void* noalloc_scratch();
 int plan_bounds(int32_t B, int64_t total_qo, int32_t Hq, int32_t Hk, int32_t D, int32_t Wd,
                 int32_t Wp, int64_t* plan_ints, int64_t* ws_bytes);
 

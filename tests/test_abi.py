@@ -331,8 +331,17 @@ def test_cascade_checks_both_levels_index_arrays():
     assert cascade(good, good, pool=None) == fi.binding.FI_ERR_INVALID_ARG
 
 
-def test_read_status_rejects_null_pointers():
-    L = fi.lib()
-    out = ctypes.c_int32()
-    assert L.fi_read_status(None, ctypes.byref(out), 0, None) == fi.binding.FI_ERR_INVALID_ARG
-    assert L.fi_read_status(16, None, 0, None) == fi.binding.FI_ERR_INVALID_ARG
+def test_read_status_rejects_a_null_status_pointer():
+    assert fi.lib().fi_read_status(16, None, 0, None) == fi.binding.FI_ERR_INVALID_ARG
+
+
+def test_noalloc_decode_refuses_plans_larger_than_its_scratch_on_the_host():
+    """The size check comes before any device call: 599 x 2 partial slots of
+    32 heads x 128 dims do not fit the 16 MiB static scratch."""
+    torch = __import__("torch")
+    plan = fi.fi_plan(None, [0, 2, 5], [3, 9], page_size=16, num_qo_heads=32, num_kv_heads=8,
+                      head_dim=128, causal=True, workers_decode=600, min_seg_pages=1)
+    params = fi.make_params(torch.bfloat16, torch.bfloat16, 32, 8, 128, 16)
+    rc = fi.lib().fi_batch_decode_paged_noalloc(plan.host_ptr(), None, ctypes.byref(params), None, None, 0,
+                                                None, None, None, None, None, None)
+    assert rc == fi.binding.FI_ERR_WORKSPACE_TOO_SMALL and "scratch" in fi.fi_last_error()
