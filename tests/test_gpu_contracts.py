@@ -14,39 +14,67 @@ from gpu_util import DeviceBatch, assert_close, note, run
 pytestmark = pytest.mark.gpu
 
 
-def _scaled_v(b, rng, big):
-    """V of every page scaled to |v| ~ big, a few entries pushed to +-6e4 and
-    a few to |v| < 2^-17 (below fp16's normal range), rounded to bf16; the
-    oracle reads the same bf16 values."""
-    v = b.kv_pool[:, 1].float()
-    v = v * big
-    flat = v.view(-1)
-    n = flat.numel()
-    hi = torch.from_numpy(rng.choice(n, n // 97, replace=False))
-    flat[hi] = torch.from_numpy(rng.choice([-6.0e4, 6.0e4], hi.numel()).astype(np.float32))
-    lo = torch.from_numpy(rng.choice(n, n // 89, replace=False))
-    flat[lo] = torch.from_numpy((rng.standard_normal(lo.numel()) * 3e-6).astype(np.float32))
-    b.kv_pool[:, 1] = v.to(b.kv_pool.dtype)
-    assert b.kv_pool[:, 1].float().abs().max() <= 65504
+def _with_v_scaled(b, factor, clamp=None):
+    """The batch with every V element times `factor` (a power of two, so bf16
+    holds the products exactly); with `clamp`, V is then clamped to +-clamp
+    and the pool kept in float64 (+-65504 is not a bf16 value), for the
+    oracle only."""
+    import copy
+    c = copy.copy(b)
+    if clamp is not None:
+        pool = b.kv_pool.double()
+        pool[:, 1] = (pool[:, 1] * factor).clamp(-clamp, clamp)
+        c.kv_pool = pool
+        return c
+    pool = b.kv_pool.clone()
+    v = pool[:, 1].float() * factor
+    pool[:, 1] = v.to(pool.dtype)
+    got = pool[:, 1].float()
+    assert bool(((got == v) | (got.isnan() & v.isnan())).all()), "scaled V must be exact in bf16"
+    c.kv_pool = pool
+    return c
 
 
 @pytest.mark.parametrize("P", [16, 3])
-def test_prefill_v_range_up_to_fp16_max(P):
-    """Prefill runs P.V with V in fp16: bf16 values of V up to 65504 in
-    magnitude (and tiny ones) stay within the tolerance of the oracle."""
+def test_prefill_carries_v_exactly_up_to_fp16_max(P):
+    """V enters the prefill P.V product as fp16.  Every step applied to V is
+    linear, so scaling V by 2^13 (|V| up to ~4e4 <= 65504, exact in fp16)
+    must scale o by exactly 2^13 and leave lse unchanged, bit for bit, while
+    the unscaled batch matches the oracle.  Scaled by 2^15, some |V| exceed
+    65504 and are clamped to +-65504 (the documented range): the output then
+    matches the oracle on V clamped to +-65504, within the bar scaled by 2^15
+    (rows of single-query requests run in the decode kernel, which keeps bf16
+    V exact: they match the oracle on the unclamped V)."""
     rng = np.random.default_rng(910 + P)
     qo = [2, 17, 70, 1, 33, 130]
     kv = [q + int(rng.integers(0, 200)) for q in qo]
     b = wl.make_batch(910 + P, qo, kv, page_size=P, num_qo_heads=32, num_kv_heads=8, head_dim=128,
-                      dtype=torch.bfloat16, causal=True)
-    _scaled_v(b, rng, 1.0e4)
+                      dtype=torch.bfloat16, causal=True, nan_poison=True)
     o_ref, l_ref = ref.attention_of(b)
-    assert np.abs(o_ref).max() > 1e3
-    dev = DeviceBatch(b)
     for wp, ms in ((None, 8), (5, 1)):
-        note(f"prefill with |V| up to 6e4, P={P}, Wp={wp}")
-        o, lse, _ = run(b, workers_decode=3, workers_prefill=wp, min_seg_pages=ms, dev=dev)
-        assert_close(o, lse, o_ref, l_ref, f"large V, P={P}, Wp={wp}")
+        note(f"prefill P={P} Wp={wp}: unit-scale V")
+        o, lse, _ = run(b, workers_decode=3, workers_prefill=wp, min_seg_pages=ms)
+        assert_close(o, lse, o_ref, l_ref, f"unit V, P={P}, Wp={wp}")
+        big = _with_v_scaled(b, 2.0 ** 13)
+        vmax = float(torch.nan_to_num(big.kv_pool[:, 1].float(), nan=0.0).abs().max())
+        assert 16384 < vmax <= 65504
+        note(f"prefill P={P} Wp={wp}: V x 2^13 (max |V| {vmax:.0f})")
+        o13, l13, _ = run(big, workers_decode=3, workers_prefill=wp, min_seg_pages=ms)
+        assert torch.equal(o13, o * 2.0 ** 13), "o must scale exactly with V"
+        assert torch.equal(l13, lse), "lse must not depend on V"
+        over = _with_v_scaled(b, 2.0 ** 15)
+        note(f"prefill P={P} Wp={wp}: V x 2^15, some |V| > 65504")
+        o15, l15, _ = run(over, workers_decode=3, workers_prefill=wp, min_seg_pages=ms)
+        # prefill rows (requests with >= 2 queries) see V clamped to +-65504;
+        # decode rows run in the decode kernel, whose P.V keeps bf16 V exact
+        s = 2.0 ** 15
+        clamped = _with_v_scaled(b, s, clamp=65504.0)
+        exact = _with_v_scaled(b, s, clamp=float("inf"))
+        pre = np.repeat(b.qo_lens >= 2, b.qo_lens)
+        oc_ref, lc_ref = ref.attention_of(clamped)
+        oe_ref, le_ref = ref.attention_of(exact)
+        assert_close(o15[pre] / s, l15[pre], oc_ref[pre] / s, lc_ref[pre], f"V x 2^15, prefill rows, P={P}")
+        assert_close(o15[~pre] / s, l15[~pre], oe_ref[~pre] / s, le_ref[~pre], f"V x 2^15, decode rows, P={P}")
 
 
 def _with_bad_ids(b, entries):
