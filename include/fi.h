@@ -78,9 +78,7 @@ typedef enum fi_dtype { FI_F32 = 0, FI_BF16 = 1 } fi_dtype;
  *   head_dim          64 or 128
  *   causal            0 or 1 (binds requests with qo_len >= 2)
  *   workers_decode, workers_prefill: persistent workers per KV head of the
- *                     decode and prefill kernels (grid = workers x KV heads);
- *                     2 (W - 1) num_kv_heads <= 65536 for each (else
- *                     FI_ERR_UNSUPPORTED: the workspace's ticket bank)
+ *                     decode and prefill kernels (grid = workers x KV heads)
  *   min_seg_pages     >= 1, smallest segment of the page stream one worker owns
  *   br_override       0 (tile rows from the mean query length) or 16/32/64/128
  *   no_split          1: one item per row, no partial slots (unsplit reference)
@@ -208,14 +206,11 @@ typedef struct fi_attn_params {
 /*
  * The float workspace (float_ws) of the run calls.  Its first
  * fi_plan_info.float_ws_bytes bytes (fi_cascade_workspace_bytes for the
- * cascade) hold a control region -- a status word and the tickets that let
- * the last worker of a split row merge its partial results -- then the
- * partial results themselves.  The control region sits at the start and has
- * a fixed size whatever the plan; it must be zero the first time a workspace
- * is used (zero-fill it once when it is allocated).  Every run call leaves the
- * tickets as it found them, so one workspace serves any number of later
- * calls and plans, in stream order.  Calls that run at the same time must not
- * share a workspace.
+ * cascade) hold a control region -- the status word and reserved words, 256
+ * bytes at the start whatever the plan -- then the partial results of split
+ * rows.  Zero-fill the control region once, when the workspace is allocated;
+ * one workspace then serves any number of later calls and plans, in stream
+ * order.  Calls that run at the same time must not share a workspace.
  *
  * Status word (word 0 of the workspace; of the cascade's workspace for both
  * of its levels): bit flags the kernels OR in and never clear.

@@ -36,7 +36,7 @@ FI_ERR_INVALID_ARG = -1
 FI_ERR_UNSUPPORTED = -2
 
 MAGIC = 0x31504946
-VERSION = 3
+VERSION = 4
 HEADER_INTS = 64
 STREAM_DESC_INTS = 20
 STREAM0_AT = 12
@@ -44,12 +44,9 @@ STREAM1_AT = 32
 WINDOW_AT = 52
 ANY_PAGES_AT = 53  # 1 if some row has visible pages
 MAX_TILE_ROWS = 128
-# workspace control region (ints): status word and padding, then one bank of
-# ticket counters per stream; its place and size do not depend on the plan
-WS_CTRL_INTS = 64
-WS_COUNTER_INTS = 65536
-WS_COUNTER_AT = (WS_CTRL_INTS, WS_CTRL_INTS + WS_COUNTER_INTS)
-WS_CONTROL_INTS = WS_CTRL_INTS + 2 * WS_COUNTER_INTS
+# workspace control region (ints): the status word, then reserved words; its
+# place and size do not depend on the plan
+WS_CONTROL_INTS = 64
 INT32_MAX = 2 ** 31 - 1
 WINDOW_MAX_TOKENS = 2 ** 30  # a windowed request needs kv_len + qo_len below this
 
@@ -93,8 +90,6 @@ def validate(B, qo_indptr, kv_indptr, kv_last_page_len, P, Hq, Hk, D, causal, W_
         return FI_ERR_INVALID_ARG, "no_split"
     if not -1 <= window_left <= INT32_MAX:
         return FI_ERR_INVALID_ARG, "window_left"
-    if 2 * (max(W_d, W_p) - 1) * Hk > WS_COUNTER_INTS:
-        return FI_ERR_UNSUPPORTED, "too many workers x KV heads for the counter bank"
     if len(kv_indptr) != B + 1 or len(kv_last_page_len) < B:
         return FI_ERR_INVALID_ARG, "array lengths"
     if qo_indptr is not None and len(qo_indptr) != B + 1:
@@ -281,7 +276,7 @@ def plan(qo_indptr, kv_indptr, kv_last_page_len, *, page_size, num_qo_heads, num
         desc = [st["W"], st["S"], st["BR"], len(st["rows"]), len(st["items"]), st["n_slots"],
                 len(st["split_rows"]), st["slot_cap"], st["off_rows"], st["off_items"],
                 st["off_wip"], st["off_merge_indptr"], st["off_split"], st["ws_off_o"],
-                st["ws_off_lse"], st["kind"], st["off_item_meta"], WS_COUNTER_AT[st["kind"]], 0, 0]
+                st["ws_off_lse"], st["kind"], st["off_item_meta"], 0, 0, 0]
         buf[at:at + STREAM_DESC_INTS] = desc
     result = dict(B=B, total_qo=sum(qo_len), G=G, ws_floats=ws_total, window_left=window_left,
                   decode=streams[0],

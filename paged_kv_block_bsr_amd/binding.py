@@ -348,8 +348,7 @@ def fi_append_paged_kv(append_k, append_v, append_indptr, kv_pool, kv_indptr, kv
 
 def workspace(nbytes: int, device="cuda") -> "torch.Tensor":
     """A float workspace of at least ``nbytes`` bytes, zero-filled: its control
-    region (status word and merge counters) must be zero when first used, and
-    the run calls leave it so."""
+    region (the status word) must be zero when first used."""
     return torch.zeros(max(int(nbytes), 4) // 4 + 64, dtype=torch.float32, device=device)
 
 

@@ -134,8 +134,6 @@ int validate(const fi_plan_in& in) {
     return set_error(FI_ERR_INVALID_ARG, "fi_plan: br_override must be 0, 16, 32, 64 or 128");
   if (in.no_split != 0 && in.no_split != 1) return set_error(FI_ERR_INVALID_ARG, "fi_plan: no_split");
   if (in.window_left < -1) return set_error(FI_ERR_INVALID_ARG, "fi_plan: window_left < -1");
-  if (2 * ((int64_t)std::max(in.workers_decode, in.workers_prefill) - 1) * in.num_kv_heads > kWsCounterInts)
-    return set_error(FI_ERR_UNSUPPORTED, "fi_plan: 2 (workers - 1) num_kv_heads exceeds %d", kWsCounterInts);
   if (B > 0 && (!in.kv_indptr || !in.kv_last_page_len))
     return set_error(FI_ERR_INVALID_ARG, "fi_plan: null index array");
   if (B == 0 && !in.kv_indptr) return set_error(FI_ERR_INVALID_ARG, "fi_plan: null kv_indptr");
@@ -162,7 +160,7 @@ int validate(const fi_plan_in& in) {
 }
 
 // Float workspace regions (float units, each padded to 64 floats = 256 B):
-// the control region (status word, ticket counters; fixed place and size),
+// the control region (status word; fixed place and size),
 // then decode partial o, decode partial lse, prefill partial o, prefill
 // partial lse.
 void ws_layout(int32_t Hq, int32_t Hk, int32_t D, int32_t Wd, int32_t Wp, int64_t off[4],
@@ -183,8 +181,6 @@ int plan_bounds(int32_t B, int64_t total_qo, int32_t Hq, int32_t Hk, int32_t D, 
                 int32_t Wp, int64_t* plan_ints, int64_t* ws_bytes) {
   if (B < 0 || total_qo < 0 || Hq < 1 || Hk < 1 || Hq % Hk || D < 1 || Wd < 1 || Wp < 1)
     return set_error(FI_ERR_INVALID_ARG, "fi_plan_bounds: bad arguments");
-  if (2 * ((int64_t)std::max(Wd, Wp) - 1) * Hk > kWsCounterInts)
-    return set_error(FI_ERR_UNSUPPORTED, "fi_plan_bounds: 2 (workers - 1) num_kv_heads exceeds %d", kWsCounterInts);
   const int64_t G = Hq / Hk;
   const int64_t rows_d = B;
   const int64_t rows_p = ceil_div(total_qo * G, 16) + B;
@@ -294,7 +290,6 @@ int build_plan(const fi_plan_in* inp, int32_t* buf, int64_t capacity, fi_plan_in
     d[S_WS_O] = (int32_t)off[k == 0 ? 0 : 2];
     d[S_WS_LSE] = (int32_t)off[k == 0 ? 1 : 3];
     d[S_KIND] = k;
-    d[S_WS_CNT] = (int32_t)kWsCounterAt[k];
     d[S_OFF_ROWS] = (int32_t)pos;
     for (const Row& r : s.rows) {
       buf[pos++] = r.req;

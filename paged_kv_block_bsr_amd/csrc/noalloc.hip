@@ -5,9 +5,9 @@
 //
 // The array lives once per GPU for the life of the process and is zero when
 // the code object is loaded; every call on a GPU shares it and keeps what the
-// last call left there.  The calls need nothing of it to start at zero except
-// the ticket counters of the control region, which every call returns to
-// zero.  Calls that overlap on one GPU race on it.
+// last call left there.  The calls need nothing of it to start at zero (the
+// status word only collects flags).  Calls that overlap on one GPU race on
+// it.
 #include <hip/hip_runtime.h>
 
 #include <mutex>

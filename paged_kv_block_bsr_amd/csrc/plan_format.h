@@ -26,11 +26,8 @@
 //
 // The float workspace starts with a control region whose place and size do
 // not depend on the plan: word 0 is the status word (bit flags the kernels OR
-// in, read and cleared by the host), then per stream kWsCounterInts int32
-// ticket counters of split rows (counter s0 * Hk + g of the split row whose
-// first slot is s0, KV head g).  Counters are zero at rest: every call leaves
-// them as it found them, so the region must be zero once, when the workspace
-// is first used.  After it, per stream, partial outputs [slot_cap][Hk][tile][D]
+// in, read and cleared by the host), the rest of its 64 words reserved and
+// zero.  After it, per stream, partial outputs [slot_cap][Hk][tile][D]
 // and partial lse [slot_cap][Hk][tile] (fp32, natural log) at the float
 // offsets recorded in the stream descriptor; tile = G for decode, 128 for
 // prefill.
@@ -40,17 +37,14 @@
 namespace fi {
 
 constexpr int32_t kPlanMagic = 0x31504946;  // "FIP1"
-constexpr int32_t kPlanVersion = 3;
+constexpr int32_t kPlanVersion = 4;
 constexpr int kHeaderInts = 64;
 constexpr int kMetaInts = 8;  // ints per item_meta record
 // item_meta fields
 enum : int { M_REQ = 0, M_KVB = 1, M_KVLEN = 2, M_QOBASE = 3, M_QOLEN = 4, M_RB = 5, M_RE = 6 };
 constexpr int kMaxTileRows = 128;
-// workspace control region (int32 words): status word, then two counter banks
-constexpr int kWsCtrlInts = 64;
-constexpr int kWsCounterInts = 65536;  // per stream: 2 (W - 1) Hk must fit
-constexpr int64_t kWsCounterAt[2] = {kWsCtrlInts, kWsCtrlInts + kWsCounterInts};
-constexpr int64_t kWsControlInts = kWsCtrlInts + 2 * (int64_t)kWsCounterInts;
+// workspace control region (int32 words): the status word, then reserved words
+constexpr int64_t kWsControlInts = 64;
 // status word bits
 constexpr int32_t kStatusBadPage = 1;  // a page id at or past pool_pages was read (and replaced by page 0)
 // A request of a windowed plan needs kv_len + qo_len below this, so that the
@@ -96,7 +90,6 @@ enum : int {
   S_WS_LSE = 14,
   S_KIND = 15,
   S_OFF_META = 16,
-  S_WS_CNT = 17,  // int32 offset in the float workspace of this stream's ticket counters
   kStreamDescInts = 20,
 };
 
