@@ -235,7 +235,7 @@ def prefill_slice(b):
 
 
 def time_batch_call(b, steps, warmup, workers_decode=0, workers_prefill=0, pool_copies=2,
-                    window_left=-1, rope_theta=0.0):
+                    window_left=-1, rope_theta=0.0, no_split=0):
     """Plan once, then time the run call (decode/prefill kernels + merges) with
     HIP events on its stream.  Returns (mean ms, plan)."""
     import torch
@@ -248,7 +248,7 @@ def time_batch_call(b, steps, warmup, workers_decode=0, workers_prefill=0, pool_
     plan = fi.fi_plan(b.qo_indptr, b.kv_indptr, b.kv_last_page_len, page_size=b.page_size,
                       num_qo_heads=b.num_qo_heads, num_kv_heads=Hk, head_dim=b.head_dim,
                       causal=b.causal, workers_decode=wd, workers_prefill=wp,
-                      window_left=window_left)
+                      window_left=window_left, no_split=no_split)
     plan_dev = plan.to_device(dev)
     i32 = lambda a: torch.from_numpy(np.asarray(a, np.int32)).to(dev)
     pools = [b.kv_pool.to(dev) for _ in range(max(1, pool_copies))]
@@ -295,6 +295,9 @@ def secondary_measurements(args):
     the headline decode figure; same kernels, other workloads)."""
     import workloads as wl
     out = {}
+    out["skewed_long_decode"] = skewed_measurements(args.side_steps)
+    out["page_order"] = page_order_measurements(args.side_steps)
+    out["plan_host"] = plan_host_times()
     b = wl.mixed_ragged_step()
     ps = prefill_slice(b)
     ms, plan = time_batch_call(ps, args.side_steps, 3)
@@ -335,6 +338,70 @@ def secondary_measurements(args):
     out["cascade"] = {"workload": "shared_prefix_cascade (64 requests, 2048-token prefix, soft-cap 30)",
                       "cascade_us": round(ms_casc * 1e3, 2), "flat_us": round(ms_flat * 1e3, 2),
                       "speedup": round(ms_flat / ms_casc, 3)}
+    return out
+
+
+def skewed_measurements(steps):
+    """Skewed long-context decode (batch 32: one 131072-token request, 31 of
+    lognormal length): the plan's equal-segment split of the long request
+    with the merge of its partial states, against the same call with every
+    row on one worker (no_split), which leaves the long request to a single
+    wave."""
+    import workloads as wl
+    sb = wl.skewed_long_decode()
+    nb = decode_bytes(sb)
+    out = {"workload": "skewed_long_decode (batch 32, one 131072-token request)", "bytes": nb}
+    for name, ns in (("split", 0), ("no_split", 1)):
+        ms, plan = time_batch_call(sb, steps, 3, no_split=ns)
+        out[name] = {"us": round(ms * 1e3, 2), "gbs": round(nb / (ms * 1e-3) / 1e9, 1),
+                     "frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "decode_items": int(plan.info.decode_items),
+                     "decode_slots": int(plan.info.decode_slots)}
+    out["split_speedup"] = round(out["no_split"]["us"] / out["split"]["us"], 2)
+    return out
+
+
+def page_order_measurements(steps):
+    """llama8b_decode with its pages randomly permuted over the pool (the
+    bench workload) and with the identity page table (request i's pages
+    contiguous, in order): how much the scattered gather costs."""
+    import workloads as wl
+    out = {"workload": "llama8b_decode call, random vs identity page table"}
+    for name, ident in (("random", False), ("identity", True)):
+        db = wl.llama8b_decode(identity_pages=ident)
+        nb = decode_bytes(db)
+        ms, _ = time_batch_call(db, steps, 3)
+        out[name] = {"us": round(ms * 1e3, 2), "gbs": round(nb / (ms * 1e-3) / 1e9, 1),
+                     "frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del db
+    return out
+
+
+def plan_host_times(reps=100):
+    """Host time of fi_plan (the CPU-side inspector), median of ``reps`` calls
+    into a preallocated buffer, for the bench workloads."""
+    import paged_kv_block_bsr_amd as fi
+    import workloads as wl
+    out = {"reps": reps}
+    for b in (wl.llama8b_decode(), wl.skewed_long_decode(), wl.mixed_ragged_step()):
+        Hk = b.num_kv_heads
+        kw = dict(page_size=b.page_size, num_qo_heads=b.num_qo_heads, num_kv_heads=Hk, head_dim=b.head_dim,
+                  causal=b.causal, workers_decode=fi.fi_default_workers(fi.FI_KIND_DECODE, NUM_CUS, Hk),
+                  workers_prefill=fi.fi_default_workers(fi.FI_KIND_PREFILL, NUM_CUS, Hk))
+        qo = b.qo_indptr
+        total_qo = int(b.total_qo)
+        cap, _ = fi.fi_plan_bounds(b.batch_size, total_qo, b.num_qo_heads, Hk, b.head_dim,
+                                   kw["workers_decode"], kw["workers_prefill"])
+        buf = np.empty(cap, np.int32)
+        ip, last = np.ascontiguousarray(b.kv_indptr, np.int32), np.ascontiguousarray(b.kv_last_page_len, np.int32)
+        ts = []
+        for _ in range(reps + 3):
+            t0 = time.perf_counter()
+            fi.fi_plan(qo, ip, last, out=buf, **kw)
+            ts.append(time.perf_counter() - t0)
+        ts = np.array(ts[3:]) * 1e6
+        out[b.name] = {"median_us": round(float(np.median(ts)), 1), "p90_us": round(float(np.percentile(ts, 90)), 1),
+                       "batch": b.batch_size, "total_qo": total_qo}
     return out
 
 
@@ -447,6 +514,24 @@ def prefill_only(args):
             "prefill_items": int(plan.info.prefill_items), "steps": args.side_steps}
 
 
+def side_only(args):
+    """One side measurement alone (``--mode mixed | cascade | skewed``)."""
+    import workloads as wl
+    if args.mode == "skewed":
+        return skewed_measurements(args.side_steps)
+    if args.mode == "mixed":
+        b = wl.mixed_ragged_step()
+        ms, _ = time_batch_call(b, args.side_steps, 3)
+        nb, fl = decode_bytes(b), prefill_flops(b)
+        return {"workload": "mixed_ragged_step (16 prefills + 48 decodes, one call)", "ms": round(ms, 4),
+                "gbs": round(nb / (ms * 1e-3) / 1e9, 1), "tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
+    cb = wl.shared_prefix_cascade()
+    ms_flat, _ = time_batch_call(cb.flat, args.side_steps, 3)
+    ms_casc = time_cascade(cb, args.side_steps, 3, min_seg1=2)
+    return {"workload": "shared_prefix_cascade (64 requests, 2048-token prefix, soft-cap 30)",
+            "cascade_us": round(ms_casc * 1e3, 2), "flat_us": round(ms_flat * 1e3, 2)}
+
+
 def time_cascade(cb, steps, warmup, min_seg0=8, min_seg1=8):
     import torch
 
@@ -516,8 +601,25 @@ def calibrate(reps=10):
     return out
 
 
-def cpu_baseline(b, nbytes, budget_s=12.0):
-    """The fp64 oracle on the host cores over the whole batch (the sample)."""
+def host_cpu():
+    """The host's CPU model (first 'model name' of /proc/cpuinfo), its
+    logical CPUs and those this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+
+
+def cpu_baseline(b, nbytes, budget_s=12.0, single_budget_s=4.0):
+    """The fp64 oracle on the host cores over the whole batch (the sample),
+    then with one thread over the first requests of the batch (the requests
+    that fit its time budget), so the per-core rate is on record too."""
     from oracle import attn as ref
 
     q64 = b.q.double().numpy()
@@ -533,10 +635,35 @@ def cpu_baseline(b, nbytes, budget_s=12.0):
         if sum(times) >= budget_s or len(times) >= 30:
             break
     t = float(np.mean(times))
-    return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": ref.num_threads(),
-            "kind": "oracle",
-            "sample": f"whole {b.name} batch (all {b.total_qo * b.num_qo_heads} query rows), "
-                      f"{len(times)} passes, mean {t:.2f} s per pass"}
+    threads = ref.num_threads()
+    out = {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": threads,
+           "kind": "oracle",
+           "sample": f"whole {b.name} batch (all {b.total_qo * b.num_qo_heads} query rows), "
+                     f"{len(times)} passes, mean {t:.2f} s per pass", **host_cpu()}
+    # one thread: decode requests 0 .. k-1, k grown until the pass takes a
+    # second or more (bytes counted for those requests alone)
+    assert b.qo_indptr is None, "the single-thread leg samples decode requests"
+    ref.set_num_threads(1)
+    try:
+        k, t1 = 1, 0.0
+        while True:
+            sub_ip = np.ascontiguousarray(b.kv_indptr[:k + 1])
+            t0 = time.perf_counter()
+            ref.attention(q64[:k], pool64, None, sub_ip, b.kv_indices, b.kv_last_page_len[:k], **kw)
+            t1 = time.perf_counter() - t0
+            if t1 >= single_budget_s / 4 or k == b.batch_size:
+                break
+            k = min(b.batch_size, 2 * k)
+        kv = b.kv_lens[:k].astype(np.int64)
+        esz = 2 if b.dtype.itemsize == 2 else 4
+        sub_bytes = (int(kv.sum()) * b.num_kv_heads * 2 * b.head_dim * esz +
+                     k * b.num_qo_heads * (2 * b.head_dim * esz + 4) +
+                     4 * (int(b.kv_indptr[k]) + 2 * k + 1))
+        out["single_thread"] = {"value": round(sub_bytes / t1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                                "sample": f"requests 0..{k - 1} of {b.name}, one pass, {t1:.2f} s"}
+    finally:
+        ref.set_num_threads(threads)
+    return out
 
 
 def main():
@@ -553,10 +680,12 @@ def main():
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the prefill / mixed / cascade side measurements")
     ap.add_argument("--side-steps", type=int, default=20)
-    ap.add_argument("--mode", default="bench", choices=["bench", "secondary", "prefill", "calibrate"],
-                    help="secondary: only the prefill / mixed / cascade measurements; "
-                         "prefill: only the prefill-slice timing (for profiling that kernel); "
-                         "calibrate: only the plain copy / streaming-sum kernels")
+    ap.add_argument("--mode", default="bench",
+                    choices=["bench", "secondary", "prefill", "mixed", "cascade", "skewed", "calibrate"],
+                    help="secondary: only the side measurements; prefill / mixed / cascade / skewed: "
+                         "only that timing (for profiling its kernels): the prefill slice, the whole "
+                         "mixed step, the cascade (and its flat equivalent), skewed_long_decode split "
+                         "and unsplit; calibrate: only the plain copy / streaming-sum kernels")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -571,6 +700,9 @@ def main():
         return
     if args.mode == "prefill":
         print(json.dumps(prefill_only(args)), flush=True)
+        return
+    if args.mode in ("mixed", "cascade", "skewed"):
+        print(json.dumps(side_only(args)), flush=True)
         return
     result, b, nbytes = run_decode_bench(args)
     if not args.no_secondary:

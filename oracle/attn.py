@@ -34,6 +34,8 @@ def lib():
             L = ctypes.CDLL(_build.LIB)
             L.oref_last_error.restype = ctypes.c_char_p
             L.oref_num_threads.restype = ctypes.c_int
+            L.oref_set_num_threads.restype = None
+            L.oref_set_num_threads.argtypes = [ctypes.c_int]
             L.oref_validate.restype = ctypes.c_int
             L.oref_validate.argtypes = [ctypes.c_int, _i32p, _i32p, _i32p, _i32p, ctypes.c_int,
                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -67,6 +69,11 @@ class OracleError(ValueError):
 def num_threads() -> int:
     """OpenMP threads the oracle runs with."""
     return int(lib().oref_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the oracle's later calls."""
+    lib().oref_set_num_threads(int(n))
 
 
 def _i32(a):

@@ -93,6 +93,15 @@ int oref_num_threads(void) {
 #endif
 }
 
+/* Set the threads of the later parallel loops (n >= 1). */
+void oref_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 static int fail(const char *msg, long long a, long long b) {
   snprintf(g_err, sizeof(g_err), "%s (%lld, %lld)", msg, a, b);
   return OREF_EINVAL;
