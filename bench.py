@@ -316,6 +316,7 @@ def secondary_measurements(args):
         "ms": round(ms, 4), "gbs": round(nb / (ms * 1e-3) / 1e9, 1),
         "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
         "roofline_frac": round(max(nb / (HBM_PEAK_GBS * 1e9), fl / (BF16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3), 4)}
+    out["prefill_page_sizes"] = prefill_page_size_measurements(ps, args.side_steps)
     out["append"] = time_append(b, args.side_steps)
     out["window"] = window_measurements(ps, args.side_steps)
     out["rope"] = rope_measurements(ps, args.side_steps)
@@ -338,6 +339,25 @@ def secondary_measurements(args):
     out["cascade"] = {"workload": "shared_prefix_cascade (64 requests, 2048-token prefix, soft-cap 30)",
                       "cascade_us": round(ms_casc * 1e3, 2), "flat_us": round(ms_flat * 1e3, 2),
                       "speedup": round(ms_flat / ms_casc, 3)}
+    return out
+
+
+def prefill_page_size_measurements(ps, steps):
+    """The prefill slice's 16 requests (same query and KV lengths) stored with
+    pages of 1, 4, 16 and 64 tokens (pages of 1 token: the column-vector
+    BSR of the pages), each batch drawn by the same generator, so only the
+    page size differs."""
+    import workloads as wl
+    fl = prefill_flops(ps)
+    out = {"workload": "mixed_ragged_step prefill requests, page size 1 / 4 / 16 / 64", "flops": fl}
+    for P in (1, 4, 16, 64):
+        b = wl.make_batch(1009, ps.qo_lens, ps.kv_lens, page_size=P, num_qo_heads=ps.num_qo_heads,
+                          num_kv_heads=ps.num_kv_heads, head_dim=ps.head_dim, dtype=ps.dtype, causal=True,
+                          name=f"prefill_slice_P{P}")
+        ms, _ = time_batch_call(b, steps, 3)
+        out[f"P{P}"] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
+        del b
+    out["P1_over_P16"] = round(out["P1"]["ms"] / out["P16"]["ms"], 3)
     return out
 
 
@@ -519,6 +539,8 @@ def side_only(args):
     import workloads as wl
     if args.mode == "skewed":
         return skewed_measurements(args.side_steps)
+    if args.mode == "pages":
+        return prefill_page_size_measurements(prefill_slice(wl.mixed_ragged_step()), args.side_steps)
     if args.mode == "mixed":
         b = wl.mixed_ragged_step()
         ms, _ = time_batch_call(b, args.side_steps, 3)
@@ -681,11 +703,12 @@ def main():
                     help="skip the prefill / mixed / cascade side measurements")
     ap.add_argument("--side-steps", type=int, default=20)
     ap.add_argument("--mode", default="bench",
-                    choices=["bench", "secondary", "prefill", "mixed", "cascade", "skewed", "calibrate"],
+                    choices=["bench", "secondary", "prefill", "mixed", "cascade", "skewed", "pages", "calibrate"],
                     help="secondary: only the side measurements; prefill / mixed / cascade / skewed: "
                          "only that timing (for profiling its kernels): the prefill slice, the whole "
                          "mixed step, the cascade (and its flat equivalent), skewed_long_decode split "
-                         "and unsplit; calibrate: only the plain copy / streaming-sum kernels")
+                         "and unsplit, the prefill slice at page sizes 1 / 4 / 16 / 64; calibrate: only "
+                         "the plain copy / streaming-sum kernels")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -701,7 +724,7 @@ def main():
     if args.mode == "prefill":
         print(json.dumps(prefill_only(args)), flush=True)
         return
-    if args.mode in ("mixed", "cascade", "skewed"):
+    if args.mode in ("mixed", "cascade", "skewed", "pages"):
         print(json.dumps(side_only(args)), flush=True)
         return
     result, b, nbytes = run_decode_bench(args)

@@ -286,15 +286,19 @@ void prefill_kernel(PrefillParams a) {
   auto raw_page = [&](const Ctx& c, int key) -> int { return c.kvi[(uint32_t)page_idx(key)]; };
   // With power-of-two pages of >= 16 tokens (FAST) a wave's 16 K keys sit
   // in one page (tiles start on 16-key boundaries), whose id is then
-  // wave-uniform, and so do a thread's 4 V keys.  K keys past t1 need no
-  // clamping beyond the page (their logits are masked; the page is
-  // valid); V keys are clamped to t1 - 1 so that masked keys still read
-  // finite values (P = 0 times a NaN would not vanish).
+  // wave-uniform, and so do a thread's 4 V keys.  With other pages (down to
+  // one token each: the column-vector BSR) lane l of every wave loads the id
+  // of tile key l -- one coalesced load per tile -- and each K or V key
+  // takes its id from that lane (ds_bpermute).  K keys past t1 need no
+  // clamping beyond the page (their logits are masked; the page is valid)
+  // with FAST pages; otherwise, and for V, keys are clamped to t1 - 1 so
+  // that masked keys still read finite values (P = 0 times a NaN would not
+  // vanish).
   struct KPages {
-    int id[FAST ? 1 : SH::KDma];
+    int id[1];
   };
-  struct VPages {
-    int id[FAST ? 1 : 4];
+  struct VPages {  // FAST: the thread's V page; otherwise unused (the ids are in KPages)
+    int id[1];
   };
   auto fetch_k = [&](const Ctx& c, int n) -> KPages {
     KPages pg;
@@ -303,8 +307,7 @@ void prefill_kernel(PrefillParams a) {
       const int pi = min(page_idx(ts + wave_u * SH::KeysPerWave), page_idx(c.t1 - 1));
       pg.id[0] = n < c.ntiles ? c.kvi[(uint32_t)pi] : 0;  // same in every lane of the wave
     } else {
-#pragma unroll
-      for (int j = 0; j < SH::KDma; ++j) pg.id[j] = n < c.ntiles ? raw_page(c, clamp_key(c, ts + k_key(j))) : 0;
+      pg.id[0] = n < c.ntiles ? raw_page(c, clamp_key(c, ts + lane)) : 0;  // tile key `lane`
     }
     return pg;
   };
@@ -312,14 +315,11 @@ void prefill_kernel(PrefillParams a) {
     VPages pg;
     const int ts = c.t0 + n * kTileK;
     const bool ok = n < c.ntiles && v_active;
-    if constexpr (FAST) {
-      pg.id[0] = ok ? raw_page(c, clamp_key(c, ts + 4 * v_kg)) : 0;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) pg.id[j] = ok ? raw_page(c, clamp_key(c, ts + 4 * v_kg + j)) : 0;
-    }
+    pg.id[0] = FAST && ok ? raw_page(c, clamp_key(c, ts + 4 * v_kg)) : 0;
     return pg;
   };
+  // the page id of tile key `key` (0 .. 63) from the coalesced ids
+  auto id_of_key = [&](const KPages& pg, int key) { return __shfl(pg.id[0], key); };
   auto dma_k = [&](const Ctx& c, int n, uint8_t* kb, const KPages& pg) {
     const int ts = c.t0 + n * kTileK;
     if constexpr (FAST) {
@@ -335,7 +335,7 @@ void prefill_kernel(PrefillParams a) {
       for (int j = 0; j < SH::KDma; ++j) {
         const int key = k_key(j);
         const int kc = clamp_key(c, ts + key);
-        const uint8_t* src = kv_head + (int64_t)checked(pg.id[j]) * page_bytes +
+        const uint8_t* src = kv_head + (int64_t)checked(id_of_key(pg, key)) * page_bytes +
                              (uint32_t)(slot_of(kc) * tok_bytes + (k_pp ^ (key & (SH::KPiecesRow - 1))) * 16);
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
                                          (FI_LDS void*)(kb + (wave_u * SH::KDma + j) * 1024), 16, 0, 0);
@@ -343,12 +343,15 @@ void prefill_kernel(PrefillParams a) {
     }
   };
   u32x4_t vreg[4] = {};
-  auto load_v = [&](const Ctx& c, int n, const VPages& pg) {
+  auto load_v = [&](const Ctx& c, int n, const KPages& pk, const VPages& pg) {
+    int vid[FAST ? 1 : 4];  // with other pages, each key's id from its lane (every lane takes part)
+#pragma unroll
+    for (int j = 0; j < (FAST ? 1 : 4); ++j) vid[j] = FAST ? pg.id[0] : id_of_key(pk, 4 * v_kg + j);
     if (v_active) {
       const int ts = c.t0 + n * kTileK;
       const uint8_t* base = kv_head + half_bytes + v_piece * 16;
       if (FAST && ts + kTileK <= c.t1) {  // whole tile valid: the 4 keys are consecutive slots of one page
-        const uint8_t* b0 = base + (uint64_t)checked(pg.id[0]) * page_bytes_u +
+        const uint8_t* b0 = base + (uint64_t)checked(vid[0]) * page_bytes_u +
                             __umul24((uint32_t)slot_of(ts + 4 * v_kg), (uint32_t)tok_bytes);
 #pragma unroll
         for (int j = 0; j < 4; ++j) vreg[j] = load16(b0 + (uint32_t)(j * tok_bytes));
@@ -356,7 +359,7 @@ void prefill_kernel(PrefillParams a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int kc = clamp_key(c, ts + 4 * v_kg + j);
-          const uint8_t* pbase = base + (uint64_t)checked(pg.id[FAST ? 0 : j]) * page_bytes_u;
+          const uint8_t* pbase = base + (uint64_t)checked(vid[FAST ? 0 : j]) * page_bytes_u;
           vreg[j] = load16(pbase + __umul24((uint32_t)slot_of(kc), (uint32_t)tok_bytes));
         }
       }
@@ -431,7 +434,7 @@ void prefill_kernel(PrefillParams a) {
     pv_ids = fetch_v(c, 0);
     if (c.ntiles > 0) {
       dma_k(c, 0, k_lds0, pk);
-      load_v(c, 0, pv_ids);
+      load_v(c, 0, pk, pv_ids);
     }
     pk = fetch_k(c, 1);
     pv_ids = fetch_v(c, 1);
@@ -638,8 +641,8 @@ void prefill_kernel(PrefillParams a) {
       }
     }
     // the next item's record has landed: the page ids of its first tile
-    // (with pages of any size, 8 ids a lane: fetched after the loop instead,
-    // as holding them through it would spill)
+    // (with other pages than FAST ones fetched after the loop instead:
+    // holding them through it spills)
     const Item nxt = uniform(nxt_raw);
     const Ctx nc = make_ctx(nxt);
     KPages npk{};
@@ -670,7 +673,7 @@ void prefill_kernel(PrefillParams a) {
       kread(kb, 0, kop0);
       kread(kb, 1, kop1);
       dma_k(cx, n + 1, kb_next, pk);
-      load_v(cx, n + 1, pv_ids);
+      load_v(cx, n + 1, pk, pv_ids);
       pk = fetch_k(cx, n + 2);
       pv_ids = fetch_v(cx, n + 2);
       qk(kop0, s0);
@@ -713,7 +716,7 @@ void prefill_kernel(PrefillParams a) {
     auto stage_only = [&](int n, auto cur) {
       constexpr bool B1 = decltype(cur)::value;
       dma_k(cx, n + 1, B1 ? k_lds0 : k_lds1, pk);
-      load_v(cx, n + 1, pv_ids);
+      load_v(cx, n + 1, pk, pv_ids);
       pk = fetch_k(cx, n + 2);
       pv_ids = fetch_v(cx, n + 2);
       store_v(B1 ? v_lds0 : v_lds1);
@@ -744,7 +747,7 @@ void prefill_kernel(PrefillParams a) {
       }
       if (nc.ntiles > 0) {
         dma_k(nc, 0, k_lds0, npk);
-        load_v(nc, 0, npv);
+        load_v(nc, 0, npk, npv);
       }
       pk = fetch_k(nc, 1);
       pv_ids = fetch_v(nc, 1);
