@@ -262,6 +262,9 @@ int fi_batch_decode_paged(const int32_t* plan_host, const int32_t* plan_dev,
  * tolerance), and larger ones are clamped to +-65504.  Keep |V| <= 65504 on
  * this path.  q and k are not narrowed (bf16 products, fp32 sums) unless the
  * rotary embedding is on (see rope_theta).
+ * With a page_size that is not a power of two >= 16, the prefill kernel
+ * needs 2 * pool_pages * page_size < 2^32 (a pool below 2^31 tokens), else
+ * FI_ERR_UNSUPPORTED before anything runs.
  */
 int fi_batch_prefill_paged(const int32_t* plan_host, const int32_t* plan_dev,
                            const fi_attn_params* params, const void* q, const void* kv_pool,

@@ -10,6 +10,11 @@ int launch_prefill(const RunArgs& r) {
     return set_error(FI_ERR_UNSUPPORTED, "prefill tiles need bf16 q / kv (fp32 runs decode rows only)");
   if ((int64_t)4 * r.P * r.Hk * r.D >= ((int64_t)1 << 32))
     return set_error(FI_ERR_UNSUPPORTED, "prefill: one page of the pool must stay below 4 GiB");
+  const bool pow2_16 = r.P >= 16 && (r.P & (r.P - 1)) == 0;
+  if (!pow2_16 && (uint64_t)2 * (uint64_t)r.pool_pages * (uint64_t)r.P >= ((uint64_t)1 << 32))
+    return set_error(FI_ERR_UNSUPPORTED,
+                     "prefill: with pages that are not a power of two >= 16 tokens, the pool must hold fewer "
+                     "than 2^31 tokens");
   PrefillParams p;
   p.plan = r.plan;
   p.q = static_cast<const uint8_t*>(r.q);

@@ -318,8 +318,15 @@ void prefill_kernel(PrefillParams a) {
     pg.id[0] = FAST && ok ? raw_page(c, clamp_key(c, ts + 4 * v_kg)) : 0;
     return pg;
   };
-  // the page id of tile key `key` (0 .. 63) from the coalesced ids
-  auto id_of_key = [&](const KPages& pg, int key) { return __shfl(pg.id[0], key); };
+  // Other pages: lane l turns the id of tile key l into that key's K row in
+  // the pool, counted in token rows (page p's K rows start at row 2 p P, its
+  // V rows P later; below 2^32 rows: checked on the host), so a K or V key
+  // needs only that lane's row (ds_bpermute) and one multiply-add.
+  auto key_rows = [&](const Ctx& c, int n, const KPages& pg) -> uint32_t {
+    const int kl = clamp_key(c, c.t0 + n * kTileK + lane);
+    return 2u * checked(pg.id[0]) * (uint32_t)P + (uint32_t)slot_of(kl);
+  };
+  auto row_addr = [&](uint32_t row) { return kv_head + (uint64_t)row * (uint32_t)tok_bytes; };
   auto dma_k = [&](const Ctx& c, int n, uint8_t* kb, const KPages& pg) {
     const int ts = c.t0 + n * kTileK;
     if constexpr (FAST) {
@@ -331,27 +338,35 @@ void prefill_kernel(PrefillParams a) {
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + k_off[j]),
                                          (FI_LDS void*)(kb + (wave_u * SH::KDma + j) * 1024), 16, 0, 0);
     } else {
+      const uint32_t rows = key_rows(c, n, pg);
 #pragma unroll
       for (int j = 0; j < SH::KDma; ++j) {
         const int key = k_key(j);
-        const int kc = clamp_key(c, ts + key);
-        const uint8_t* src = kv_head + (int64_t)checked(id_of_key(pg, key)) * page_bytes +
-                             (uint32_t)(slot_of(kc) * tok_bytes + (k_pp ^ (key & (SH::KPiecesRow - 1))) * 16);
+        const uint8_t* src = row_addr(__shfl(rows, key)) + (k_pp ^ (key & (SH::KPiecesRow - 1))) * 16;
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
                                          (FI_LDS void*)(kb + (wave_u * SH::KDma + j) * 1024), 16, 0, 0);
       }
     }
+    (void)ts;
   };
   u32x4_t vreg[4] = {};
   auto load_v = [&](const Ctx& c, int n, const KPages& pk, const VPages& pg) {
-    int vid[FAST ? 1 : 4];  // with other pages, each key's id from its lane (every lane takes part)
+    if constexpr (!FAST) {  // each key's V row from its lane (every lane takes part)
+      const uint32_t rows = key_rows(c, n, pk) + (uint32_t)P;
+      uint32_t vrow[4];
 #pragma unroll
-    for (int j = 0; j < (FAST ? 1 : 4); ++j) vid[j] = FAST ? pg.id[0] : id_of_key(pk, 4 * v_kg + j);
+      for (int j = 0; j < 4; ++j) vrow[j] = __shfl(rows, 4 * v_kg + j);
+      if (v_active) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vreg[j] = load16(row_addr(vrow[j]) + v_piece * 16);
+      }
+      return;
+    }
     if (v_active) {
       const int ts = c.t0 + n * kTileK;
       const uint8_t* base = kv_head + half_bytes + v_piece * 16;
-      if (FAST && ts + kTileK <= c.t1) {  // whole tile valid: the 4 keys are consecutive slots of one page
-        const uint8_t* b0 = base + (uint64_t)checked(vid[0]) * page_bytes_u +
+      if (ts + kTileK <= c.t1) {  // whole tile valid: the 4 keys are consecutive slots of one page
+        const uint8_t* b0 = base + (uint64_t)checked(pg.id[0]) * page_bytes_u +
                             __umul24((uint32_t)slot_of(ts + 4 * v_kg), (uint32_t)tok_bytes);
 #pragma unroll
         for (int j = 0; j < 4; ++j) vreg[j] = load16(b0 + (uint32_t)(j * tok_bytes));
@@ -359,7 +374,7 @@ void prefill_kernel(PrefillParams a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int kc = clamp_key(c, ts + 4 * v_kg + j);
-          const uint8_t* pbase = base + (uint64_t)checked(vid[FAST ? 0 : j]) * page_bytes_u;
+          const uint8_t* pbase = base + (uint64_t)checked(pg.id[0]) * page_bytes_u;
           vreg[j] = load16(pbase + __umul24((uint32_t)slot_of(kc), (uint32_t)tok_bytes));
         }
       }

@@ -307,6 +307,25 @@ def test_run_calls_need_the_pool_and_page_table_when_the_plan_reads_pages():
 
 
 @fake_addresses
+def test_prefill_with_other_pages_refuses_pools_of_2_31_tokens_or_more():
+    """Pages that are not a power of two >= 16 tokens: the prefill kernel
+    addresses the pool in 32-bit token rows, so a pool of 2^31 tokens or more
+    is refused on the host."""
+    torch = __import__("torch")
+    L = fi.lib()
+    plan = fi.fi_plan([0, 4], [0, 2], [3], page_size=3, num_qo_heads=8, num_kv_heads=2, head_dim=128,
+                      causal=True, workers_decode=2, workers_prefill=2)
+    params = fi.make_params(torch.bfloat16, torch.bfloat16, 8, 2, 128, 3)
+
+    def prefill(pool_pages):
+        return L.fi_batch_prefill_paged(plan.host_ptr(), 16, ctypes.byref(params), 16, 16, pool_pages, 16, 16,
+                                        16, 16, 16, None, 16, plan.float_ws_bytes, None)
+
+    assert prefill((1 << 31) // 3 + 1) == fi.binding.FI_ERR_UNSUPPORTED
+    assert "2^31 tokens" in fi.fi_last_error()
+
+
+@fake_addresses
 def test_cascade_checks_both_levels_index_arrays():
     torch = __import__("torch")
     L = fi.lib()
