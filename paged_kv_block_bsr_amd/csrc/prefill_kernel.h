@@ -691,6 +691,11 @@ void prefill_kernel(PrefillParams a) {
       load_v(cx, n + 1, pk, pv_ids);
       pk = fetch_k(cx, n + 2);
       pv_ids = fetch_v(cx, n + 2);
+      // The products and the softmax run at a raised wave priority, the V
+      // conversion and the wait for the next tile at the normal one: while
+      // this workgroup's waves wait, the other workgroup's waves on the same
+      // SIMDs win the issue slots (slice call 0.1382 ms against 0.1427).
+      __builtin_amdgcn_s_setprio(3);
       qk(kop0, s0);
       prepare(n, 0, s0, mask_tag, mw0);
       // QK(b1) + softmax(b0) + V(b0) reads
@@ -706,6 +711,7 @@ void prefill_kernel(PrefillParams a) {
       exps(s1, p1);
       // PV(b1) + the conversion of the next V tile
       pv(vop1, p1);
+      __builtin_amdgcn_s_setprio(0);
       store_v(vb_next);
       FI_WAIT_VMCNT(0);
       __syncthreads();
