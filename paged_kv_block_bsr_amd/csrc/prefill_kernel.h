@@ -289,8 +289,8 @@ void prefill_kernel(PrefillParams a) {
   // wave-uniform, and so do a thread's 4 V keys.  With other pages (down to
   // one token each: the column-vector BSR) lane l of every wave loads the id
   // of tile key l -- one coalesced load per tile -- and each K or V key
-  // takes its id from that lane (ds_bpermute).  K keys past t1 need no
-  // clamping beyond the page (their logits are masked; the page is valid)
+  // gets its pool row from that lane (key_rows below).  K keys past t1 need
+  // no clamping beyond the page (their logits are masked; the page is valid)
   // with FAST pages; otherwise, and for V, keys are clamped to t1 - 1 so
   // that masked keys still read finite values (P = 0 times a NaN would not
   // vanish).
@@ -328,8 +328,8 @@ void prefill_kernel(PrefillParams a) {
   };
   auto row_addr = [&](uint32_t row) { return kv_head + (uint64_t)row * (uint32_t)tok_bytes; };
   auto dma_k = [&](const Ctx& c, int n, uint8_t* kb, const KPages& pg) {
-    const int ts = c.t0 + n * kTileK;
     if constexpr (FAST) {
+      const int ts = c.t0 + n * kTileK;
       const int pid = __builtin_amdgcn_readfirstlane(pg.id[0]);
       const uint8_t* base = kv_head + (int64_t)checked(pid) * page_bytes +
                             slot_of(ts + wave_u * SH::KeysPerWave) * tok_bytes;
@@ -347,7 +347,6 @@ void prefill_kernel(PrefillParams a) {
                                          (FI_LDS void*)(kb + (wave_u * SH::KDma + j) * 1024), 16, 0, 0);
       }
     }
-    (void)ts;
   };
   u32x4_t vreg[4] = {};
   auto load_v = [&](const Ctx& c, int n, const KPages& pk, const VPages& pg) {
