@@ -167,3 +167,49 @@ def test_mixed_step_graph_replays_with_changing_lengths():
              ([1, 1, 1, 1, 1, 1], [31, 71, 6, 301, 65, 10])]
     splits = _run_steps(7002, steps, W_d=8, W_p=6, mixed=True, min_seg=1)
     assert splits[0][1] == 0 and splits[1][1] > 0 and splits[3][1] == 0, splits
+
+
+def test_cascade_graph_replays_bit_exactly():
+    """fi_cascade (level 0, level 1, their split merges and the final merge)
+    captured once with graph_safe and replayed: replays, with eager work and
+    synchronisation between them, match the eager call bit for bit and the
+    fp64 oracle of the flat batch."""
+    cb = wl.shared_prefix_cascade(num_requests=24, prefix_len=640, seed=7003)
+    l0, l1 = cb.level0, cb.level1
+    kw = dict(page_size=l0.page_size, num_qo_heads=l0.num_qo_heads, num_kv_heads=l0.num_kv_heads,
+              head_dim=l0.head_dim, workers_decode=48, workers_prefill=16, min_seg_pages=2)
+    plan0 = fi.fi_plan(l0.qo_indptr, l0.kv_indptr, l0.kv_last_page_len, causal=False, **kw)
+    plan1 = fi.fi_plan(l1.qo_indptr, l1.kv_indptr, l1.kv_last_page_len, causal=l1.causal, **kw)
+    assert plan0.info.prefill_slots > 0 and plan1.info.decode_slots > 0  # both levels split and merge
+    i32 = lambda a: torch.from_numpy(np.asarray(a, np.int32).copy()).cuda()
+    dev0 = (plan0.to_device(), i32(l0.qo_indptr), i32(l0.kv_indptr), i32(l0.kv_indices), i32(l0.kv_last_page_len))
+    dev1 = (plan1.to_device(), None if l1.qo_indptr is None else i32(l1.qo_indptr), i32(l1.kv_indptr),
+            i32(l1.kv_indices), i32(l1.kv_last_page_len))
+    q, pool = l0.q.cuda(), l0.kv_pool.cuda()
+
+    def call(graph_safe, o, lse, ws):
+        params = fi.make_params(l0.dtype, l0.dtype, l0.num_qo_heads, l0.num_kv_heads, l0.head_dim,
+                                l0.page_size, l0.sm_scale, l0.soft_cap, graph_safe=graph_safe)
+        fi.fi_cascade(plan0, *dev0, plan1, *dev1, params, q, pool, o, lse, ws)
+
+    nbytes = fi.fi_cascade_workspace_bytes(plan0, plan1)
+    o_g, l_g = torch.zeros_like(q), torch.zeros(q.shape[:2], dtype=torch.float32, device="cuda")
+    ws_g = fi.workspace(nbytes)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(True, o_g, l_g, ws_g)
+    torch.cuda.synchronize()
+    o_e, l_e = torch.zeros_like(q), torch.zeros(q.shape[:2], dtype=torch.float32, device="cuda")
+    ws_e = fi.workspace(nbytes)
+    o_ref, l_ref = ref.attention_of(cb.flat)
+    for k in range(3):
+        note(f"cascade graph replay {k}")
+        o_g.zero_()
+        l_g.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        call(False, o_e, l_e, ws_e)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_e), f"replay {k}: output differs from the eager call"
+        assert torch.equal(l_g, l_e), f"replay {k}: lse differs from the eager call"
+        assert_close(o_g.float().cpu(), l_g.cpu(), o_ref, l_ref, f"cascade replay {k}")
