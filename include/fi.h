@@ -79,7 +79,10 @@ typedef enum fi_dtype { FI_F32 = 0, FI_BF16 = 1 } fi_dtype;
  *   causal            0 or 1 (binds requests with qo_len >= 2)
  *   workers_decode, workers_prefill: persistent workers per KV head of the
  *                     decode and prefill kernels (grid = workers x KV heads)
- *   min_seg_pages     >= 1, smallest segment of the page stream one worker owns
+ *   min_seg_pages     >= 1, smallest segment of a stream one worker owns, in
+ *                     cost units: a decode row costs its visible pages, a
+ *                     prefill tile its visible pages plus ceil(512 /
+ *                     page_size) for its fixed work
  *   br_override       0 (tile rows from the mean query length) or 16/32/64/128
  *   no_split          1: one item per row, no partial slots (unsplit reference)
  *   window_left       -1: no window.  >= 0: sliding-window attention, the
@@ -116,7 +119,7 @@ typedef struct fi_plan_info {
   int64_t plan_ints;        /* int32 words written to the plan buffer */
   int64_t float_ws_bytes;   /* float workspace the run calls need */
   int32_t decode_rows, decode_items, decode_slots, decode_segment_pages;
-  int32_t prefill_rows, prefill_items, prefill_slots, prefill_segment_pages;
+  int32_t prefill_rows, prefill_items, prefill_slots, prefill_segment_pages; /* segments in cost units */
   int32_t prefill_tile_rows; /* BR: packed (token, head) rows per prefill tile */
 } fi_plan_info;
 

@@ -10,21 +10,27 @@ it and merge the partials by log-sum-exp composition (FlashInfer paper page,
 ahead of time and balances deterministically with a cost model (talk page,
 "Runtime Scheduler for Dynamic Problem Shapes"); the query tile size is picked
 from the batch's average query length (paper page, JIT paragraph).  Where they
-stop, this module takes the plainest reading (cost = KV pages; equal-size
-contiguous segments of the concatenated page stream, one per worker) and
-spells out every step:
+stop, this module takes the plainest reading (cost = KV pages plus a fixed
+charge per work item; workers filled in row order up to one segment size
+each) and spells out every step:
 
 P1 validate; P2 per-request pages, kv_len, qo_len; P3 classify requests
 (qo_len 0: nothing, 1: a decode row, >= 2: prefill tiles); P4 prefill tile
 size BR; P5 rows in request order, each with its first visible page fp
 (0, or with a sliding window of w keys the page of the first key the row's
 earliest query sees, max(0, kv_len - qo_len + tok_lo - w)) and its visible
-pages counted from fp; P6 per stream, cost C = sum of visible
-pages, segment size S = max(min_seg_pages, ceil(C / W)), row r occupies stream
-positions [c_r, c_r + vis_r), worker w owns [w S, (w + 1) S); P7 one item per
-(row, worker) overlap, a row without visible pages gets one empty item, and an
-item's pages are the overlap shifted by fp - c_r (pages of its request); P8
-rows with k >= 2 items get k consecutive partial slots; P9 emit int32 arrays.
+pages counted from fp; P6 per stream, an item (a row's pages on one worker)
+costs h plus its pages, with h = 0 for decode rows and h = ceil(512 / P) for
+a prefill tile (a fixed charge for the work a tile does whatever its length:
+loading its queries, writing its output rows, starting the item); C = the sum
+over rows of h + vis_r; P7 fill workers in row order: a worker that has
+already used S - h or more of its segment S takes nothing more, a row that
+does not fit is cut where the worker is full and its rest starts a new item
+on the next worker, the last worker takes what is left, and a row without
+visible pages is one empty item on the current worker; S is the smallest
+value >= max(h + min_seg_pages, ceil(C / W)) at which the last worker's cost
+stays within S; item pages are shifted by fp (pages of its request); P8 rows
+with k >= 2 items get k consecutive partial slots; P9 emit int32 arrays.
 
 Parity against the pages: unpinned (they print no plan); the tests pin this
 module by invariants and by an independent brute-force partition.
@@ -36,7 +42,7 @@ FI_ERR_INVALID_ARG = -1
 FI_ERR_UNSUPPORTED = -2
 
 MAGIC = 0x31504946
-VERSION = 4
+VERSION = 5
 HEADER_INTS = 64
 STREAM_DESC_INTS = 20
 STREAM0_AT = 12
@@ -49,6 +55,7 @@ MAX_TILE_ROWS = 128
 WS_CONTROL_INTS = 64
 INT32_MAX = 2 ** 31 - 1
 WINDOW_MAX_TOKENS = 2 ** 30  # a windowed request needs kv_len + qo_len below this
+TILE_COST_KEYS = 512  # fixed cost of a prefill tile, in keys (rounded up to pages)
 
 
 def _ceil_div(a: int, b: int) -> int:
@@ -117,24 +124,44 @@ def validate(B, qo_indptr, kv_indptr, kv_last_page_len, P, Hq, Hk, D, causal, W_
     return FI_OK, ""
 
 
-def _partition(rows_vis, W, S, no_split):
-    """P6-P8 for one stream.  rows_vis[r] = visible pages of row r.
-    Returns (items sorted by (worker, row), wip, merge_indptr, split_rows)."""
-    items = []  # (w, r, page_begin, page_end)
+def _fill(rows_vis, W, S, h):
+    """P7 for one segment size S: returns (items as (w, r, page_begin,
+    page_end), the last worker's cost)."""
+    items = []
+    w, used = 0, 0
+    for r, vis in enumerate(rows_vis):
+        if w < W - 1 and S - used <= h:
+            w, used = w + 1, 0
+        if vis == 0:
+            items.append((w, r, 0, 0))
+            used += h
+            continue
+        done = 0
+        while done < vis:
+            room = vis - done if w == W - 1 else S - used - h
+            n = min(vis - done, room)
+            items.append((w, r, done, done + n))
+            used += h + n
+            done += n
+            if done < vis:
+                w, used = w + 1, 0
+    return items, used
+
+
+def _partition(rows_vis, W, min_seg_pages, no_split, h=0):
+    """P6-P8 for one stream.  rows_vis[r] = visible pages of row r, h = the
+    fixed cost of an item.  Returns (S, items sorted by (worker, row), wip,
+    merge_indptr, split_rows)."""
+    C = sum(h + v for v in rows_vis)
+    S = max(h + min_seg_pages, _ceil_div(C, W))
     if no_split:
-        for r, vis in enumerate(rows_vis):
-            items.append((r % W, r, 0, vis))
+        items = [(r % W, r, 0, vis) for r, vis in enumerate(rows_vis)]
     else:
-        c = 0
-        for r, vis in enumerate(rows_vis):
-            if vis == 0:
-                items.append((min(c // S, W - 1), r, 0, 0))
-            else:
-                for w in range(c // S, (c + vis - 1) // S + 1):
-                    lo = max(c, w * S)
-                    hi = min(c + vis, (w + 1) * S)
-                    items.append((w, r, lo - c, hi - c))
-            c += vis
+        while True:  # smallest S that fits: try S, S + 1, ...
+            items, last = _fill(rows_vis, W, S, h)
+            if last <= S:
+                break
+            S += 1
     items.sort(key=lambda it: (it[0], it[1]))
     # P8: rows split over k >= 2 items get k consecutive slots (row order,
     # then page_begin order inside the row).
@@ -160,7 +187,7 @@ def _partition(rows_vis, W, S, no_split):
     for w in range(W):
         wip[w + 1] += wip[w]
     out_items = [(r, pb, pe, slot_of_item[idx]) for idx, (w, r, pb, pe) in enumerate(items)]
-    return out_items, wip, merge_indptr, split_rows
+    return S, out_items, wip, merge_indptr, split_rows
 
 
 def plan(qo_indptr, kv_indptr, kv_last_page_len, *, page_size, num_qo_heads, num_kv_heads,
@@ -231,12 +258,13 @@ def plan(qo_indptr, kv_indptr, kv_last_page_len, *, page_size, num_qo_heads, num
     for kind, rows, fps, W, tile in ((0, rows_d, fp_d, workers_decode, G),
                                      (1, rows_p, fp_p, workers_prefill, BR)):
         vis = [r[3] for r in rows]
-        C = sum(vis)
-        S = max(min_seg_pages, _ceil_div(C, W))
-        items, wip, merge_indptr, split_rows = _partition(vis, W, S, no_split)
+        h = 0 if kind == 0 else _ceil_div(TILE_COST_KEYS, P)
+        S, items, wip, merge_indptr, split_rows = _partition(vis, W, min_seg_pages, no_split, h)
+        if S > INT32_MAX:
+            return FI_ERR_INVALID_ARG, "segment too large"
         # item pages are request pages: shift by the row's first visible page
         items = [(r, fps[r] + pb, fps[r] + pe, slot) for (r, pb, pe, slot) in items]
-        streams.append(dict(kind=kind, W=W, S=S, BR=tile, rows=rows, first_page=fps, items=items, wip=wip,
+        streams.append(dict(kind=kind, W=W, S=S, h=h, BR=tile, rows=rows, first_page=fps, items=items, wip=wip,
                             merge_indptr=merge_indptr, split_rows=split_rows,
                             n_slots=merge_indptr[-1],
                             slot_cap=cap_d if kind == 0 else cap_p,

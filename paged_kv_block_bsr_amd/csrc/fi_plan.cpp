@@ -1,14 +1,17 @@
-// fi_plan.cpp -- the CPU-side inspector: splits each step's KV page stream
-// into equal segments, one per persistent worker, and records where partial
+// fi_plan.cpp -- the CPU-side inspector: splits each step's work into
+// segments of equal cost, one per persistent worker, and records where partial
 // results go (FlashInfer paper page, "Load balancing that survives CUDA
 // graphs"; talk page, "Runtime Scheduler for Dynamic Problem Shapes": a cost
 // model inspected ahead of time, deterministic balance, no tail wave).
 //
-// Cost model: one unit per visible KV page of a row.  Rows are decode rows
-// (one query token, the G heads of a KV head packed together) and prefill
-// tiles of BR packed (token, head) rows; BR follows the batch's mean packed
-// query length (paper page, the query tile size of the JIT paragraph).  The
-// two kinds form separate streams because they run in different kernels.
+// Cost model: one unit per visible KV page of a work item, plus, for an item
+// of a prefill tile, a fixed charge of kTileCostKeys keys rounded up to pages
+// for the work it does whatever its length (loading the tile's queries,
+// writing its output rows or partial results).  Rows are decode rows (one query token, the G heads
+// of a KV head packed together) and prefill tiles of BR packed (token, head)
+// rows; BR follows the batch's mean packed query length (paper page, the query
+// tile size of the JIT paragraph).  The two kinds form separate streams
+// because they run in different kernels.
 //
 // Host only: no HIP call.  O(B + rows + items + W) time.
 #include <climits>
@@ -33,6 +36,12 @@ inline int32_t next_pow2(int64_t x) {
 
 inline int64_t align64(int64_t n) { return ceil_div(n, 64) * 64; }
 
+// Fixed cost of a prefill work item, in keys (rounded up to pages).  On the
+// 16 causal prefills of the mixed ragged step (page 16) the prefill kernel
+// takes 0.139 ms with no charge, 0.127-0.129 ms at 512 keys (32 pages), 0.133
+// at 256 and 0.128-0.131 from 384 to 1024.
+constexpr int64_t kTileCostKeys = 512;
+
 struct Row {
   int32_t req, rb, re, vis;
   int32_t fp;  // first visible page (not part of the rows array)
@@ -45,16 +54,72 @@ struct StreamPlan {
   std::vector<int32_t> item_row, item_pb, item_pe, item_slot, wip, merge, split;
 };
 
-void partition(StreamPlan& st, int32_t min_seg, bool no_split) {
+// Greedy fill with segment size S: rows in order go to worker 0 until its
+// cost reaches S, then to worker 1, and so on.  Each item (a row's pages on
+// one worker) costs h plus its pages.  A worker with S - h or more already
+// used takes nothing more; a row that does not fit is cut where the worker
+// is full and continues on the next worker, which pays h again.  The last
+// worker takes whatever is left.  Returns whether the last worker's cost
+// stays within S.  With `emit`, records items (sorted by worker, then row,
+// because workers never decrease) and their count per row.
+bool fill(StreamPlan& st, int64_t S, int64_t h, bool emit, std::vector<int32_t>& nitems_row) {
+  const int32_t W = st.W;
+  int64_t w = 0, u = 0;  // current worker and its cost so far
+  auto add = [&](int64_t r, int64_t pb, int64_t pe) {
+    u += h + (pe - pb);
+    if (!emit) return;
+    st.item_row.push_back((int32_t)r);
+    st.item_pb.push_back((int32_t)pb);
+    st.item_pe.push_back((int32_t)pe);
+    st.wip[w + 1] += 1;
+    nitems_row[r] += 1;
+  };
+  for (int64_t r = 0; r < (int64_t)st.rows.size(); ++r) {
+    const int64_t vis = st.rows[r].vis;
+    if (w < W - 1 && S - u <= h) w += 1, u = 0;
+    if (vis == 0) {
+      add(r, 0, 0);
+      continue;
+    }
+    int64_t pb = 0;
+    for (;;) {
+      const int64_t take = (w == W - 1) ? vis - pb : std::min<int64_t>(vis - pb, S - u - h);
+      add(r, pb, pb + take);
+      pb += take;
+      if (pb == vis) break;
+      w += 1, u = 0;
+    }
+  }
+  return u <= S;
+}
+
+// P6 - P8 for one stream.  S is the smallest segment, at least min_seg pages
+// past the fixed cost and at least the mean cost per worker, at which the
+// greedy fill fits W workers.  lo + 2 h always fits: each worker but the last
+// is left holding at least S - h, of which at most h repeats the fixed cost
+// of a cut row, so the last one gets at most C - (W - 1)(S - 2 h) + h <= S.
+int partition(StreamPlan& st, int32_t min_seg, bool no_split, int64_t h) {
   const int32_t W = st.W;
   const int64_t nrows = (int64_t)st.rows.size();
   int64_t C = 0;
-  for (const Row& r : st.rows) C += r.vis;
-  st.S = (int32_t)std::max<int64_t>(min_seg, ceil_div(C, W));
-  const int64_t S = st.S;
+  for (const Row& r : st.rows) C += h + r.vis;
+  int64_t lo = std::max<int64_t>(h + min_seg, ceil_div(C, W)), hi = lo + 2 * h;
+  std::vector<int32_t> nitems_row(nrows, 0);
+  if (!no_split) {
+    while (lo < hi) {  // feasibility only grows with S
+      const int64_t mid = lo + (hi - lo) / 2;
+      if (fill(st, mid, h, false, nitems_row))
+        hi = mid;
+      else
+        lo = mid + 1;
+    }
+  }
+  if (lo > INT32_MAX)
+    return set_error(FI_ERR_INVALID_ARG, "fi_plan: segment of %lld cost units too large", (long long)lo);
+  st.S = (int32_t)lo;
+  const int64_t S = lo;
   st.wip.assign(W + 1, 0);
   st.merge.assign(nrows + 1, 0);
-  std::vector<int32_t> nitems_row(nrows, 0);
 
   if (no_split) {
     // one item per row on worker r mod W: counting sort by worker keeps rows ascending
@@ -65,39 +130,16 @@ void partition(StreamPlan& st, int32_t min_seg, bool no_split) {
     st.item_pb.assign(n, 0);
     st.item_pe.assign(n, 0);
     st.item_slot.assign(n, -1);
-    std::vector<int32_t> fill(st.wip.begin(), st.wip.end() - 1);
+    std::vector<int32_t> at(st.wip.begin(), st.wip.end() - 1);
     for (int64_t r = 0; r < nrows; ++r) {
-      int32_t k = fill[r % W]++;
+      int32_t k = at[r % W]++;
       st.item_row[k] = (int32_t)r;
       st.item_pe[k] = st.rows[r].vis;
     }
-    return;  // merge stays all-zero, no split rows
+    return FI_OK;  // merge stays all-zero, no split rows
   }
 
-  // Rows in order, each cut at worker boundaries: the generated order is
-  // already sorted by (worker, row) because worker indices never decrease.
-  int64_t c = 0;
-  for (int64_t r = 0; r < nrows; ++r) {
-    const int64_t vis = st.rows[r].vis;
-    if (vis == 0) {
-      int64_t w = std::min<int64_t>(c / S, W - 1);
-      st.item_row.push_back((int32_t)r);
-      st.item_pb.push_back(0);
-      st.item_pe.push_back(0);
-      st.wip[w + 1] += 1;
-      nitems_row[r] = 1;
-    } else {
-      for (int64_t w = c / S; w <= (c + vis - 1) / S; ++w) {
-        int64_t lo = std::max<int64_t>(c, w * S), hi = std::min<int64_t>(c + vis, (w + 1) * S);
-        st.item_row.push_back((int32_t)r);
-        st.item_pb.push_back((int32_t)(lo - c));
-        st.item_pe.push_back((int32_t)(hi - c));
-        st.wip[w + 1] += 1;
-        nitems_row[r] += 1;
-      }
-    }
-    c += vis;
-  }
+  fill(st, S, h, true, nitems_row);
   for (int32_t w = 0; w < W; ++w) st.wip[w + 1] += st.wip[w];
   // slots: rows with k >= 2 items get k consecutive slots, in page order
   for (int64_t r = 0; r < nrows; ++r) {
@@ -113,6 +155,7 @@ void partition(StreamPlan& st, int32_t min_seg, bool no_split) {
     prev_row = r;
     if (nitems_row[r] >= 2) st.item_slot[k] = st.merge[r] + j;
   }
+  return FI_OK;
 }
 
 int validate(const fi_plan_in& in) {
@@ -257,7 +300,10 @@ int build_plan(const fi_plan_in* inp, int32_t* buf, int64_t capacity, fi_plan_in
     }
   }
   // P6 - P8
-  for (auto& s : st) partition(s, in.min_seg_pages, in.no_split != 0);
+  rc = partition(st[0], in.min_seg_pages, in.no_split != 0, 0);
+  if (rc) return rc;
+  rc = partition(st[1], in.min_seg_pages, in.no_split != 0, ceil_div(kTileCostKeys, P));
+  if (rc) return rc;
 
   int64_t off[4], ws_total;
   ws_layout(Hq, Hk, D, in.workers_decode, in.workers_prefill, off, &ws_total);

@@ -37,7 +37,7 @@
 namespace fi {
 
 constexpr int32_t kPlanMagic = 0x31504946;  // "FIP1"
-constexpr int32_t kPlanVersion = 4;
+constexpr int32_t kPlanVersion = 5;
 constexpr int kHeaderInts = 64;
 constexpr int kMetaInts = 8;  // ints per item_meta record
 // item_meta fields

@@ -1,16 +1,17 @@
 """Pins of the plan oracle (oracle/plan_ref.py).
 
 The pages print no plan, so the oracle is pinned by what its rules imply:
-- a brute-force partition that walks the page stream one position at a time
-  and cuts it wherever the owning worker or the row changes;
+- a brute-force partition that hands the pages out one at a time, each
+  work item paying the stream's fixed cost, and cuts a row wherever the
+  owning worker changes; the segment size is the smallest this walk fits;
 - invariants: every row's visible pages are covered exactly once and in order,
-  no worker holds more than S pages, items <= rows + W - 1, slots <= 2 (W - 1),
-  slot numbering, worker item ranges;
+  no worker's cost (fixed cost per item plus pages) exceeds S, items <= rows
+  + W - 1, slots <= 2 (W - 1), slot numbering, worker item ranges;
+- a worked example of the prefill fixed cost;
 - the tile-size rule on the worked values (mean query length 960 -> 128,
   256 -> 128, 12 -> 16);
 - validation codes.
 """
-import bisect
 
 import numpy as np
 import pytest
@@ -28,29 +29,29 @@ def _random_case(rng, B, max_qo, max_kv, P, causal):
     return qo_indptr, kv_indptr, last, qo, kv
 
 
-def brute_force_items(vis, W, S):
-    """Walk the stream position by position; emit (w, r, pb, pe) runs."""
-    c = np.concatenate([[0], np.cumsum(vis)]).astype(np.int64)
+def brute_force_items(vis, W, S, h=0):
+    """Hand the pages out one at a time: a row starts with the fixed cost h
+    on the current worker (the next one if not even one page would fit after
+    it), each page goes where the running cost stays within S, and a page
+    that does not fit opens a new item, with its own h, on the next worker;
+    the last worker takes all that is left.  Returns (w, r, pb, pe) runs and
+    the last worker's cost."""
     out = []
+    w, used = 0, 0
     for r, v in enumerate(vis):
-        if v == 0:
-            out.append((min(int(c[r]) // S, W - 1), r, 0, 0))
-    C = int(c[-1])
-    run = None
-    for pos in range(C):
-        r = bisect.bisect_right(c, pos) - 1
-        while vis[r] == 0:
-            r += 1
-        w = pos // S
-        if run and run[0] == w and run[1] == r:
-            run[3] += 1
-        else:
-            if run:
+        if w < W - 1 and used + h >= S:
+            w, used = w + 1, 0
+        run = [w, r, 0, 0]
+        used += h
+        for page in range(v):
+            if w < W - 1 and used + 1 > S:
                 out.append(tuple(run))
-            run = [w, r, pos - int(c[r]), pos - int(c[r]) + 1]
-    if run:
+                w, used = w + 1, h
+                run = [w, r, page, page]
+            run[3] += 1
+            used += 1
         out.append(tuple(run))
-    return sorted(out, key=lambda t: (t[0], t[1]))
+    return sorted(out, key=lambda t: (t[0], t[1])), used
 
 
 def _check_stream(st, no_split):
@@ -91,14 +92,19 @@ def _check_stream(st, no_split):
         for k, (r, pb, pe, slot) in enumerate(items):
             assert owner[k] == r % W
     else:
-        load = np.zeros(W, int)
+        h = st["tile_cost"]
+        load = np.zeros(W, int)  # an item costs h plus its pages
         for k, (r, pb, pe, slot) in enumerate(items):
-            load[owner[k]] += pe - pb
+            load[owner[k]] += h + pe - pb
         assert load.max(initial=0) <= S
         assert len(items) <= len(rows) + W - 1
         assert st["merge_indptr"][-1] <= 2 * (W - 1)
-        assert S == max(st["min_seg"], -(-sum(vis) // W))
-        bf = brute_force_items(vis, W, S)
+        lo = max(h + st["min_seg"], -(-(sum(vis) + h * len(vis)) // W))
+        assert lo <= S <= lo + 2 * h
+        # S is the smallest segment at which the walk fits the W workers
+        assert S == lo or brute_force_items(vis, W, S - 1, h)[1] > S - 1
+        bf, last = brute_force_items(vis, W, S, h)
+        assert last <= S
         got = sorted([(owner[k], r, pb - fps[r], pe - fps[r]) for k, (r, pb, pe, slot) in enumerate(items)],
                      key=lambda t: (t[0], t[1]))
         assert got == bf
@@ -122,8 +128,9 @@ def test_plan_oracle_invariants_and_brute_force(seed):
                         workers_decode=Wd, workers_prefill=Wp, min_seg_pages=ms,
                         no_split=no_split)
     assert code == 0, res
-    for st in (res["decode"], res["prefill"]):
+    for st, h in ((res["decode"], 0), (res["prefill"], -(-512 // P))):
         st["min_seg"] = ms
+        st["tile_cost"] = h
         _check_stream(st, no_split)
     qo_eff = np.ones(B, int) if decode_only else qo
     assert len(res["decode"]["rows"]) == int((qo_eff == 1).sum())
@@ -171,6 +178,36 @@ def test_long_request_is_split_into_equal_segments():
     long_items = [it for it in st["items"] if it[0] == 0]
     assert len(long_items) == -(-8192 // S)
     assert all(pe - pb == S for (_, pb, pe, _) in long_items[:-1])
+
+
+def test_prefill_tile_fixed_cost_worked_example():
+    """Five one-tile prefill requests of 64, 8, 8, 8 and 8 pages (page 16, so
+    an item's fixed cost is 512 / 16 = 32) on two workers.  Costs 96, 40, 40,
+    40, 40 sum to 256, so S >= 128.  Below S = 136 worker 0 can hold the long
+    tile and at most part of the second, whose rest pays 32 again on worker
+    1 (33 + 120 > 135); at 136 worker 0 holds tiles 0 and 1 whole (136) and
+    worker 1 the other three (120): nothing is cut.  Pages alone (S = 48)
+    would cut the long tile in two."""
+    P = 16
+    npg = np.array([64, 8, 8, 8, 8])
+    kv_indptr = np.concatenate([[0], np.cumsum(npg)])
+    last = np.full(5, P)
+    qo_indptr = np.arange(6) * 16
+    kw = dict(page_size=P, num_qo_heads=1, num_kv_heads=1, head_dim=64, causal=False,
+              workers_decode=1, workers_prefill=2, min_seg_pages=1, br_override=16)
+    code, res = pr.plan(qo_indptr, kv_indptr, last, **kw)
+    assert code == 0, res
+    st = res["prefill"]
+    assert st["S"] == 136
+    assert st["wip"] == [0, 2, 5]
+    assert st["items"] == [(0, 0, 64, -1), (1, 0, 8, -1), (2, 0, 8, -1), (3, 0, 8, -1), (4, 0, 8, -1)]
+    assert st["split_rows"] == [] and st["n_slots"] == 0
+    # the decode stream keeps pages as its only cost: 64 + 4 * 8 pages of
+    # single-query requests on two workers give S = 48 and cut the long row
+    code, res = pr.plan(None, kv_indptr, last, **dict(kw, workers_decode=2))
+    st = res["decode"]
+    assert st["S"] == 48 and st["split_rows"] == [0]
+    assert st["items"][:2] == [(0, 0, 48, 0), (0, 48, 64, 1)]
 
 
 @pytest.mark.parametrize("bad,code", [
@@ -288,8 +325,9 @@ def test_window_rows_cover_exactly_the_pages_their_queries_see(seed):
                         no_split=no_split, window_left=window)
     assert code == 0, res
     assert res["buf"][pr.WINDOW_AT] == window
-    for st in (res["decode"], res["prefill"]):
+    for st, h in ((res["decode"], 0), (res["prefill"], -(-512 // P))):
         st["min_seg"] = ms
+        st["tile_cost"] = h
         _check_stream(st, no_split)
         covered = {r: set() for r in range(len(st["rows"]))}
         for (r, pb, pe, slot) in st["items"]:
