@@ -79,10 +79,11 @@ typedef enum fi_dtype { FI_F32 = 0, FI_BF16 = 1 } fi_dtype;
  *   causal            0 or 1 (binds requests with qo_len >= 2)
  *   workers_decode, workers_prefill: persistent workers per KV head of the
  *                     decode and prefill kernels (grid = workers x KV heads)
- *   min_seg_pages     >= 1, smallest segment of a stream one worker owns, in
- *                     cost units: a decode row costs its visible pages, a
- *                     prefill tile its visible pages plus ceil(512 /
- *                     page_size) for its fixed work
+ *   min_seg_pages     >= 1, pages past its fixed cost in the smallest segment
+ *                     of a stream one worker owns.  Cost units: a work item
+ *                     (a row's pages on one worker) costs its pages plus
+ *                     ceil(32 / page_size) for a decode row, ceil(512 /
+ *                     page_size) for a prefill tile
  *   br_override       0 (tile rows from the mean query length) or 16/32/64/128
  *   no_split          1: one item per row, no partial slots (unsplit reference)
  *   window_left       -1: no window.  >= 0: sliding-window attention, the

@@ -20,9 +20,10 @@ size BR; P5 rows in request order, each with its first visible page fp
 (0, or with a sliding window of w keys the page of the first key the row's
 earliest query sees, max(0, kv_len - qo_len + tok_lo - w)) and its visible
 pages counted from fp; P6 per stream, an item (a row's pages on one worker)
-costs h plus its pages, with h = 0 for decode rows and h = ceil(512 / P) for
-a prefill tile (a fixed charge for the work a tile does whatever its length:
-loading its queries, writing its output rows, starting the item); C = the sum
+costs h plus its pages, with h = ceil(32 / P) for a decode row and
+h = ceil(512 / P) for a prefill tile (a fixed charge for the work an item does
+whatever its length: loading its queries, writing its output rows or partial
+state, starting the item); C = the sum
 over rows of h + vis_r; P7 fill workers in row order: a worker that has
 already used S - h or more of its segment S takes nothing more, a row that
 does not fit is cut where the worker is full and its rest starts a new item
@@ -55,7 +56,8 @@ MAX_TILE_ROWS = 128
 WS_CONTROL_INTS = 64
 INT32_MAX = 2 ** 31 - 1
 WINDOW_MAX_TOKENS = 2 ** 30  # a windowed request needs kv_len + qo_len below this
-TILE_COST_KEYS = 512  # fixed cost of a prefill tile, in keys (rounded up to pages)
+TILE_COST_KEYS = 512  # fixed cost of a prefill work item, in keys (rounded up to pages)
+DECODE_ITEM_COST_KEYS = 32  # fixed cost of a decode work item, in keys (rounded up to pages)
 
 
 def _ceil_div(a: int, b: int) -> int:
@@ -258,7 +260,7 @@ def plan(qo_indptr, kv_indptr, kv_last_page_len, *, page_size, num_qo_heads, num
     for kind, rows, fps, W, tile in ((0, rows_d, fp_d, workers_decode, G),
                                      (1, rows_p, fp_p, workers_prefill, BR)):
         vis = [r[3] for r in rows]
-        h = 0 if kind == 0 else _ceil_div(TILE_COST_KEYS, P)
+        h = _ceil_div(DECODE_ITEM_COST_KEYS if kind == 0 else TILE_COST_KEYS, P)
         S, items, wip, merge_indptr, split_rows = _partition(vis, W, min_seg_pages, no_split, h)
         if S > INT32_MAX:
             return FI_ERR_INVALID_ARG, "segment too large"

@@ -128,7 +128,7 @@ def test_plan_oracle_invariants_and_brute_force(seed):
                         workers_decode=Wd, workers_prefill=Wp, min_seg_pages=ms,
                         no_split=no_split)
     assert code == 0, res
-    for st, h in ((res["decode"], 0), (res["prefill"], -(-512 // P))):
+    for st, h in ((res["decode"], -(-32 // P)), (res["prefill"], -(-512 // P))):
         st["min_seg"] = ms
         st["tile_cost"] = h
         _check_stream(st, no_split)
@@ -173,11 +173,14 @@ def test_long_request_is_split_into_equal_segments():
     code, res = pr.plan(None, kv_indptr, last, page_size=P, num_qo_heads=32, num_kv_heads=8,
                         head_dim=128, causal=True, workers_decode=128, workers_prefill=1)
     st = res["decode"]
-    S = st["S"]
-    assert S == -(-int(npg.sum()) // 128)
+    S, h = st["S"], 2  # a decode item's fixed cost: 32 keys = 2 pages
+    lo = -(-(int(npg.sum()) + h * len(npg)) // 128)
+    assert lo <= S <= lo + 2 * h
+    # the long request starts on an empty worker: every piece but the last
+    # fills a whole segment with pages after its fixed cost
     long_items = [it for it in st["items"] if it[0] == 0]
-    assert len(long_items) == -(-8192 // S)
-    assert all(pe - pb == S for (_, pb, pe, _) in long_items[:-1])
+    assert len(long_items) == -(-8192 // (S - h))
+    assert all(pe - pb == S - h for (_, pb, pe, _) in long_items[:-1])
 
 
 def test_prefill_tile_fixed_cost_worked_example():
@@ -186,8 +189,8 @@ def test_prefill_tile_fixed_cost_worked_example():
     40, 40 sum to 256, so S >= 128.  Below S = 136 worker 0 can hold the long
     tile and at most part of the second, whose rest pays 32 again on worker
     1 (33 + 120 > 135); at 136 worker 0 holds tiles 0 and 1 whole (136) and
-    worker 1 the other three (120): nothing is cut.  Pages alone (S = 48)
-    would cut the long tile in two."""
+    worker 1 the other three (120): nothing is cut.  The same requests as
+    single queries (decode items, a fixed cost of 2) cut the long row."""
     P = 16
     npg = np.array([64, 8, 8, 8, 8])
     kv_indptr = np.concatenate([[0], np.cumsum(npg)])
@@ -202,12 +205,15 @@ def test_prefill_tile_fixed_cost_worked_example():
     assert st["wip"] == [0, 2, 5]
     assert st["items"] == [(0, 0, 64, -1), (1, 0, 8, -1), (2, 0, 8, -1), (3, 0, 8, -1), (4, 0, 8, -1)]
     assert st["split_rows"] == [] and st["n_slots"] == 0
-    # the decode stream keeps pages as its only cost: 64 + 4 * 8 pages of
-    # single-query requests on two workers give S = 48 and cut the long row
+    # decode items pay 32 / 16 = 2: single-query requests of the same pages
+    # cost 66, 10, 10, 10, 10 (sum 106, S >= 53).  At 53 worker 0 takes 51
+    # pages of the long row, and worker 1 its other 13 plus 2, then 40: 55.
+    # At 54 worker 0 takes 52 and worker 1 2 + 12 + 40 = 54: the long row is
+    # cut after page 52.
     code, res = pr.plan(None, kv_indptr, last, **dict(kw, workers_decode=2))
     st = res["decode"]
-    assert st["S"] == 48 and st["split_rows"] == [0]
-    assert st["items"][:2] == [(0, 0, 48, 0), (0, 48, 64, 1)]
+    assert st["S"] == 54 and st["split_rows"] == [0]
+    assert st["items"][:2] == [(0, 0, 52, 0), (0, 52, 64, 1)]
 
 
 @pytest.mark.parametrize("bad,code", [
@@ -325,7 +331,7 @@ def test_window_rows_cover_exactly_the_pages_their_queries_see(seed):
                         no_split=no_split, window_left=window)
     assert code == 0, res
     assert res["buf"][pr.WINDOW_AT] == window
-    for st, h in ((res["decode"], 0), (res["prefill"], -(-512 // P))):
+    for st, h in ((res["decode"], -(-32 // P)), (res["prefill"], -(-512 // P))):
         st["min_seg"] = ms
         st["tile_cost"] = h
         _check_stream(st, no_split)
