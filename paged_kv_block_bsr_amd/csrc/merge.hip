@@ -37,6 +37,12 @@ constexpr int kMergeRows = 16;  // packed rows per merge block (grid z covers a 
 // folds its slots into a running (max, sum, weighted o) state as it reads
 // them -- lse and o of a slot are loaded together, so a block needs one
 // round trip to memory -- and the group states are composed through LDS.
+// kBatch: slots a thread loads before folding them.  Decode rows of a long
+// request are split into hundreds of slots, which batches of 4 fold with
+// fewer waits (skewed_long_decode: merge 13.3 -> 11.0 us); prefill tiles are
+// split in two or three, where the batch's registers cost more than they
+// save (slice call 0.1266 -> 0.1287 ms), so their merge folds one at a time.
+template <int kBatch>
 __global__ __launch_bounds__(kThreads) void merge_partials_kernel(MergeParams a) {
   const int32_t* sd = a.plan + a.stream_at;
   const int task = blockIdx.x;
@@ -97,24 +103,44 @@ __global__ __launch_bounds__(kThreads) void merge_partials_kernel(MergeParams a)
     f32x4_t acc[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) acc[v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-    for (int s = s0 + sg; s < s1; s += ngroups) {
-      const int64_t pr = ((int64_t)s * a.Hk + g) * stride + r0 + rr;
-      const float x = wl[pr];
-      f32x4_t vv[NV];
+    // Slots s, s + ngroups, ... in batches of kBatch: a batch's loads are
+    // issued together (a row split over hundreds of slots would otherwise
+    // wait for each slot in turn), then folded with one rescale.  Batch
+    // members past the row's last slot load nothing and count as lse -inf,
+    // weight 0.
+    for (int s = s0 + sg; s < s1; s += kBatch * ngroups) {
+      float x[kBatch];
+      f32x4_t vv[kBatch][NV];
 #pragma unroll
-      for (int v = 0; v < NV; ++v) vv[v] = *reinterpret_cast<const f32x4_t*>(wo + pr * D + 4 * (NV * c + v));
-      if (x > m) {  // a new running max: rescale what is there (exp(-inf) = 0 on the first slot)
-        const float r = __expf(m - x);
+      for (int b = 0; b < kBatch; ++b) {
+        const int sb = s + b * ngroups;
+        x[b] = neg_inf();
+#pragma unroll
+        for (int v = 0; v < NV; ++v) vv[b][v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (sb < s1) {
+          const int64_t pr = ((int64_t)sb * a.Hk + g) * stride + r0 + rr;
+          x[b] = wl[pr];
+#pragma unroll
+          for (int v = 0; v < NV; ++v) vv[b][v] = *reinterpret_cast<const f32x4_t*>(wo + pr * D + 4 * (NV * c + v));
+        }
+      }
+      float mb = x[0];
+#pragma unroll
+      for (int b = 1; b < kBatch; ++b) mb = fmaxf(mb, x[b]);
+      if (mb > m) {  // a new running max: rescale what is there (exp(-inf) = 0 on the first batch)
+        const float r = __expf(m - mb);
 #pragma unroll
         for (int v = 0; v < NV; ++v) acc[v] *= r;
         l *= r;
-        m = x;
+        m = mb;
       }
-      const float w = x == neg_inf() ? 0.f : __expf(x - m);
 #pragma unroll
-      for (int v = 0; v < NV; ++v) acc[v] += w * vv[v];
-      l += w;
+      for (int b = 0; b < kBatch; ++b) {
+        const float w = x[b] == neg_inf() ? 0.f : __expf(x[b] - m);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[v] += w * vv[b][v];
+        l += w;
+      }
     }
     if (ngroups > 1) {
 #pragma unroll
@@ -204,7 +230,10 @@ int launch_merge_partials(const RunArgs& r) {
   // decode rows hold G <= 8 packed rows; prefill tiles up to 128 (8 blocks of 16)
   const int z = r.stream_at == H_STREAM0 ? 1 : kMaxTileRows / kMergeRows;
   dim3 grid(std::max(1, r.max_tasks), r.Hk, z), block(kThreads);
-  hipLaunchKernelGGL(merge_partials_kernel, grid, block, 0, (hipStream_t)r.hip_stream, p);
+  if (r.stream_at == H_STREAM0)
+    hipLaunchKernelGGL(merge_partials_kernel<4>, grid, block, 0, (hipStream_t)r.hip_stream, p);
+  else
+    hipLaunchKernelGGL(merge_partials_kernel<1>, grid, block, 0, (hipStream_t)r.hip_stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(FI_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
   return FI_OK;
