@@ -535,8 +535,10 @@ def prefill_only(args):
 
 
 def side_only(args):
-    """One side measurement alone (``--mode mixed | cascade | skewed``)."""
+    """One side measurement alone (``--mode mixed | cascade | skewed | pages | append``)."""
     import workloads as wl
+    if args.mode == "append":
+        return time_append(wl.mixed_ragged_step(), args.side_steps)
     if args.mode == "skewed":
         return skewed_measurements(args.side_steps)
     if args.mode == "pages":
@@ -703,8 +705,9 @@ def main():
                     help="skip the prefill / mixed / cascade side measurements")
     ap.add_argument("--side-steps", type=int, default=20)
     ap.add_argument("--mode", default="bench",
-                    choices=["bench", "secondary", "prefill", "mixed", "cascade", "skewed", "pages", "calibrate"],
-                    help="secondary: only the side measurements; prefill / mixed / cascade / skewed: "
+                    choices=["bench", "secondary", "prefill", "mixed", "cascade", "skewed", "pages", "append",
+                             "calibrate"],
+                    help="secondary: only the side measurements; prefill / mixed / cascade / skewed / pages / append: "
                          "only that timing (for profiling its kernels): the prefill slice, the whole "
                          "mixed step, the cascade (and its flat equivalent), skewed_long_decode split "
                          "and unsplit, the prefill slice at page sizes 1 / 4 / 16 / 64; calibrate: only "
@@ -724,7 +727,7 @@ def main():
     if args.mode == "prefill":
         print(json.dumps(prefill_only(args)), flush=True)
         return
-    if args.mode in ("mixed", "cascade", "skewed", "pages"):
+    if args.mode in ("mixed", "cascade", "skewed", "pages", "append"):
         print(json.dumps(side_only(args)), flush=True)
         return
     result, b, nbytes = run_decode_bench(args)
