@@ -143,13 +143,15 @@ int run_plan(RunArgs a, const int32_t* ph, bool with_prefill, bool graph_safe) {
     return set_error(FI_ERR_UNSUPPORTED, "prefill tiles need bf16 q / kv");
   const bool dec = graph_safe || ph[H_STREAM0 + S_NROWS] != 0;
   const bool pre = with_prefill && (graph_safe ? a.dtype == FI_BF16 : ph[H_STREAM1 + S_NROWS] != 0);
+  // merge grids: one block row per split row of this plan, or the bound W - 1
+  // when the launch must serve every later plan (graph capture)
   a.stream_at = H_STREAM0;
   a.workers = ph[H_STREAM0 + S_W];
-  a.max_tasks = a.workers - 1;
+  a.max_tasks = graph_safe ? a.workers - 1 : ph[H_STREAM0 + S_NSPLIT];
   RunArgs b = a;
   b.stream_at = H_STREAM1;
   b.workers = ph[H_STREAM1 + S_W];
-  b.max_tasks = b.workers - 1;
+  b.max_tasks = graph_safe ? b.workers - 1 : ph[H_STREAM1 + S_NSPLIT];
   if (dec && (rc = launch_decode(a))) return rc;
   if (pre && (rc = launch_prefill(b))) return rc;
   if (dec && (graph_safe || ph[H_STREAM0 + S_NSPLIT] != 0) && (rc = launch_merge_partials(a))) return rc;

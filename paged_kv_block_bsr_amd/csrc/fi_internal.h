@@ -58,7 +58,7 @@ struct RunArgs {
   float soft_cap;
   fi_dtype dtype, out_dtype;
   int32_t workers;              // grid.x of this stream's kernel
-  int32_t max_tasks;            // merge kernel: grid.x bound (W - 1)
+  int32_t max_tasks;            // merge kernel grid.x: split rows of the plan, or W - 1 (graph_safe)
   int32_t stream_at;            // H_STREAM0 or H_STREAM1
   void* hip_stream;
 };

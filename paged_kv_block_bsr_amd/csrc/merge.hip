@@ -3,10 +3,11 @@
 // merge_partials: for every row the plan split over k >= 2 workers, combine
 // the k partial (o, lse) slots into the final output (serving-engine page,
 // "FlashDecoding: Parallel KV Split", the merge step; paper page, partial
-// results merged with the log-sum-exp composition).  Fixed grid
-// (workers - 1, KV heads): block x takes the x-th split row of the stream,
-// or exits when there is none, so the launch shape never depends on the
-// batch.
+// results merged with the log-sum-exp composition).  Grid (split rows of
+// the plan, KV heads, 16-row blocks): block x takes the x-th split row of
+// the stream.  A call made for graph capture launches the bound, workers -
+// 1, instead, and blocks past the stream's split rows exit, so the captured
+// launch serves every later plan.
 //
 // merge_state: the two-way merge of the cascade (serving-engine page,
 // "Cascade Attention for Shared Prefixes", merge_state).
