@@ -363,7 +363,7 @@ def prefill_page_size_measurements(ps, steps):
 
 def skewed_measurements(steps):
     """Skewed long-context decode (batch 32: one 131072-token request, 31 of
-    lognormal length): the plan's equal-segment split of the long request
+    lognormal length): the plan's split of the long request into segments of equal cost
     with the merge of its partial states, against the same call with every
     row on one worker (no_split), which leaves the long request to a single
     wave."""
