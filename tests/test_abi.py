@@ -132,6 +132,8 @@ def test_fi_plan_bit_exact_on_named_workloads(name, monkeypatch):
     (dict(num_qo_heads=48, num_kv_heads=3), fi.binding.FI_ERR_UNSUPPORTED),
     (dict(workers_decode=0), fi.binding.FI_ERR_INVALID_ARG),
     (dict(min_seg_pages=0), fi.binding.FI_ERR_INVALID_ARG),
+    # a segment of more than 2^31 - 1 cost units (min_seg plus the fixed cost)
+    (dict(min_seg_pages=2 ** 31 - 1), fi.binding.FI_ERR_INVALID_ARG),
     (dict(br_override=24), fi.binding.FI_ERR_INVALID_ARG),
     (dict(kv_last_page_len=[0, 3]), fi.binding.FI_ERR_INVALID_ARG),
     (dict(kv_last_page_len=[5, 3]), fi.binding.FI_ERR_INVALID_ARG),
