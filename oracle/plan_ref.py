@@ -43,7 +43,7 @@ FI_ERR_INVALID_ARG = -1
 FI_ERR_UNSUPPORTED = -2
 
 MAGIC = 0x31504946
-VERSION = 5
+VERSION = 6
 HEADER_INTS = 64
 STREAM_DESC_INTS = 20
 STREAM0_AT = 12
@@ -287,6 +287,11 @@ def plan(qo_indptr, kv_indptr, kv_last_page_len, *, page_size, num_qo_heads, num
         buf.extend(st["merge_indptr"])
         st["off_split"] = len(buf)
         buf.extend(st["split_rows"])
+        # per split row: its packed rows, query base and first slot
+        st["off_split_rec"] = len(buf)
+        for r in st["split_rows"]:
+            req, rb, re, _ = st["rows"][r]
+            buf.extend([rb, re, req if qo_indptr is None else qo_indptr[req], st["merge_indptr"][r]])
         # per-item copy of what a kernel needs about the item's request and
         # row, so that one load per item replaces a chain of dependent ones
         st["item_meta"] = []
@@ -306,7 +311,7 @@ def plan(qo_indptr, kv_indptr, kv_last_page_len, *, page_size, num_qo_heads, num
         desc = [st["W"], st["S"], st["BR"], len(st["rows"]), len(st["items"]), st["n_slots"],
                 len(st["split_rows"]), st["slot_cap"], st["off_rows"], st["off_items"],
                 st["off_wip"], st["off_merge_indptr"], st["off_split"], st["ws_off_o"],
-                st["ws_off_lse"], st["kind"], st["off_item_meta"], 0, 0, 0]
+                st["ws_off_lse"], st["kind"], st["off_item_meta"], st["off_split_rec"], 0, 0]
         buf[at:at + STREAM_DESC_INTS] = desc
     result = dict(B=B, total_qo=sum(qo_len), G=G, ws_floats=ws_total, window_left=window_left,
                   decode=streams[0],

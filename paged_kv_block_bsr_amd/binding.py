@@ -35,7 +35,7 @@ FI_KIND_PREFILL = 1
 H_MAGIC, H_SIZE, H_BATCH, H_TOTAL_QO, H_CAUSAL, H_WS_FLOATS = 0, 2, 3, 4, 9, 11
 H_STREAM0, H_STREAM1 = 12, 32
 (S_W, S_SEG, S_TILE, S_NROWS, S_NITEMS, S_NSLOTS, S_NSPLIT, S_SLOTCAP, S_OFF_ROWS, S_OFF_ITEMS,
- S_OFF_WIP, S_OFF_MERGE, S_OFF_SPLIT, S_WS_O, S_WS_LSE, S_KIND, S_OFF_META) = range(17)
+ S_OFF_WIP, S_OFF_MERGE, S_OFF_SPLIT, S_WS_O, S_WS_LSE, S_KIND, S_OFF_META, S_OFF_SREC) = range(18)
 
 EXPORTS = ["fi_plan", "fi_plan_bounds", "fi_batch_decode_paged", "fi_batch_prefill_paged",
            "fi_merge_state", "fi_cascade", "fi_cascade_workspace_bytes", "fi_append_paged_kv",
@@ -390,5 +390,6 @@ def decode_plan_buffer(buf) -> dict:
             wip=b[d[S_OFF_WIP]:d[S_OFF_WIP] + W + 1].tolist(),
             merge_indptr=b[d[S_OFF_MERGE]:d[S_OFF_MERGE] + nr + 1].tolist(),
             split_rows=b[d[S_OFF_SPLIT]:d[S_OFF_SPLIT] + ns].tolist(),
-            item_meta=[tuple(x) for x in b[d[S_OFF_META]:d[S_OFF_META] + 8 * ni].reshape(-1, 8).tolist()])
+            item_meta=[tuple(x) for x in b[d[S_OFF_META]:d[S_OFF_META] + 8 * ni].reshape(-1, 8).tolist()],
+            split_records=[tuple(x) for x in b[d[S_OFF_SREC]:d[S_OFF_SREC] + 4 * ns].reshape(-1, 4).tolist()])
     return out

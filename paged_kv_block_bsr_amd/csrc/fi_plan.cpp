@@ -234,7 +234,7 @@ int plan_bounds(int32_t B, int64_t total_qo, int32_t Hq, int32_t Hk, int32_t D, 
   const int64_t rows_p = ceil_div(total_qo * G, 16) + B;
   auto stream_ints = [](int64_t rows, int64_t W) {
     int64_t items = rows + W - 1;
-    return 4 * rows + (4 + kMetaInts) * items + (W + 1) + (rows + 1) + rows;
+    return 4 * rows + (4 + kMetaInts) * items + (W + 1) + (rows + 1) + 5 * rows;
   };
   if (plan_ints) *plan_ints = kHeaderInts + stream_ints(rows_d, Wd) + stream_ints(rows_p, Wp);
   int64_t off[4], total;
@@ -319,7 +319,7 @@ int build_plan(const fi_plan_in* inp, int32_t* buf, int64_t capacity, fi_plan_in
   int64_t need = kHeaderInts;
   for (auto& s : st)
     need += 4 * (int64_t)s.rows.size() + (4 + kMetaInts) * (int64_t)s.item_row.size() + (s.W + 1) +
-            ((int64_t)s.rows.size() + 1) + (int64_t)s.split.size();
+            ((int64_t)s.rows.size() + 1) + 5 * (int64_t)s.split.size();
   if (!buf || capacity < need)
     return set_error(FI_ERR_WORKSPACE_TOO_SMALL, "fi_plan: plan buffer holds %lld ints, needs %lld",
                      (long long)capacity, (long long)need);
@@ -362,6 +362,14 @@ int build_plan(const fi_plan_in* inp, int32_t* buf, int64_t capacity, fi_plan_in
     for (int32_t v : s.merge) buf[pos++] = v;
     d[S_OFF_SPLIT] = (int32_t)pos;
     for (int32_t v : s.split) buf[pos++] = v;
+    d[S_OFF_SREC] = (int32_t)pos;
+    for (int32_t r : s.split) {
+      const Row& row = s.rows[r];
+      buf[pos++] = row.rb;
+      buf[pos++] = row.re;
+      buf[pos++] = in.qo_indptr ? in.qo_indptr[row.req] : row.req;
+      buf[pos++] = s.merge[r];
+    }
     d[S_OFF_META] = (int32_t)pos;
     for (int64_t j = 0; j < ni; ++j) {
       const Row& r = s.rows[s.item_row[j]];

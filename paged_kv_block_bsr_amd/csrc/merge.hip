@@ -21,7 +21,6 @@ constexpr int kThreads = 256;
 
 struct MergeParams {
   const int32_t* plan;
-  const int32_t* qo_indptr;
   uint8_t* o;
   float* lse;
   const float* ws;
@@ -47,23 +46,21 @@ template <int kBatch>
 __global__ __launch_bounds__(kThreads) void merge_partials_kernel(MergeParams a) {
   const int32_t* sd = a.plan + a.stream_at;
   const int task = blockIdx.x;
-  if (task >= sd[S_NSPLIT]) return;
+  const int n_split = sd[S_NSPLIT];
+  if (task >= n_split) return;
   const int g = blockIdx.y;
-  const int32_t* rows = a.plan + sd[S_OFF_ROWS];
-  const int32_t* merge = a.plan + sd[S_OFF_MERGE];
-  const int row = a.plan[sd[S_OFF_SPLIT] + task];
-  const int req = rows[4 * row + 0];
-  const int rb = rows[4 * row + 1];
-  const int re = rows[4 * row + 2];
+  // the split row's record: packed rows, query base, first slot; its slots
+  // end where the next record's begin (the last at the stream's slot count)
+  const int32_t* rec = a.plan + sd[S_OFF_SREC] + 4 * task;
+  const int rb = rec[0], re = rec[1], qbase = rec[2], s0 = rec[3];
+  const int s1 = task + 1 < n_split ? rec[4 + 3] : sd[S_NSLOTS];
   const int r0 = kMergeRows * blockIdx.z;
   if (r0 >= re - rb) return;
   const int nr = min(kMergeRows, re - rb - r0);
-  const int s0 = merge[row], s1 = merge[row + 1];
   // partial layout [slot][Hk][stride][D]; stride = G for decode rows, 128 for tiles
   const int stride = sd[S_KIND] == 0 ? a.G : kMaxTileRows;
   const float* wo = a.ws + sd[S_WS_O];
   const float* wl = a.ws + sd[S_WS_LSE];
-  const int qbase = a.qo_indptr ? a.qo_indptr[req] : req;
   const int D = a.D, G = a.G;
   const int tid = threadIdx.x;
 
@@ -218,7 +215,6 @@ __global__ __launch_bounds__(kThreads) void merge_state_kernel(const uint8_t* va
 int launch_merge_partials(const RunArgs& r) {
   MergeParams p;
   p.plan = r.plan;
-  p.qo_indptr = r.qo_indptr;
   p.o = static_cast<uint8_t*>(r.o);
   p.lse = r.lse;
   p.ws = r.ws;

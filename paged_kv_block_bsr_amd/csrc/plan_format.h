@@ -2,7 +2,7 @@
 // kernels read from device memory.
 //
 // The buffer starts with a fixed header, then per stream (0 = decode rows,
-// 1 = prefill tiles) five arrays:
+// 1 = prefill tiles) seven arrays:
 //   rows   [n_rows][4]  {request, packed_row_begin, packed_row_end, visible_pages}
 //                        (counted from the row's first visible page)
 //   items  [n_items][4] {row, page_begin, page_end, slot}  (slot -1: write the
@@ -10,6 +10,10 @@
 //   wip    [W+1]        items of worker w are items[wip[w] .. wip[w+1])
 //   merge  [n_rows+1]   slots of row r are merge[r] .. merge[r+1]
 //   split  [n_split]    rows with two or more items, in row order
+//   srec   [n_split][4] {packed_row_begin, packed_row_end, qo_base,
+//                        first slot} of each split row (its slots end where
+//                        the next record's begin, the last at n_slots), so
+//                        the merge reads one record instead of a chain
 //   meta   [n_items][8] {request, kv_indptr[request], kv_len, qo_base, qo_len,
 //                        packed_row_begin, packed_row_end, 0} of each item's
 //                        request and row (qo_base = qo_indptr[request], or the
@@ -37,7 +41,7 @@
 namespace fi {
 
 constexpr int32_t kPlanMagic = 0x31504946;  // "FIP1"
-constexpr int32_t kPlanVersion = 5;
+constexpr int32_t kPlanVersion = 6;
 constexpr int kHeaderInts = 64;
 constexpr int kMetaInts = 8;  // ints per item_meta record
 // item_meta fields
@@ -90,6 +94,7 @@ enum : int {
   S_WS_LSE = 14,
   S_KIND = 15,
   S_OFF_META = 16,
+  S_OFF_SREC = 17,
   kStreamDescInts = 20,
 };
 

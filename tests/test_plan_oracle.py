@@ -295,6 +295,34 @@ def test_item_meta_describes_each_items_request_and_row(seed):
             assert res["buf"][off:off + 8 * len(st["item_meta"])] == [x for m in st["item_meta"] for x in m]
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_split_records_describe_each_split_row(seed):
+    """Record k restates the k-th split row for the merge: its packed rows,
+    its query base (from the raw qo_indptr) and its first slot; its slots end
+    where the next record's begin, the last at the stream's slot count."""
+    rng = np.random.default_rng(700 + seed)
+    P = int(rng.choice([1, 3, 16]))
+    B = int(rng.integers(1, 12))
+    qo_indptr, kv_indptr, last, qo, kv = _random_case(rng, B, 40, 400, P, True)
+    Wd, Wp = int(rng.integers(1, 24)), int(rng.integers(1, 24))
+    for qi in (None, qo_indptr):
+        code, res = pr.plan(qi, kv_indptr, last, page_size=P, num_qo_heads=8, num_kv_heads=2,
+                            head_dim=64, causal=True, workers_decode=Wd, workers_prefill=Wp,
+                            min_seg_pages=1)
+        assert code == 0, res
+        buf = res["buf"]
+        for at, st in ((pr.STREAM0_AT, res["decode"]), (pr.STREAM1_AT, res["prefill"])):
+            off, n = buf[at + 17], len(st["split_rows"])
+            recs = [tuple(buf[off + 4 * k:off + 4 * k + 4]) for k in range(n)]
+            mi = st["merge_indptr"]
+            ends = [rec[3] for rec in recs[1:]] + [st["n_slots"]]
+            for k, r in enumerate(st["split_rows"]):
+                req, rb, re, _ = st["rows"][r]
+                qb = req if qi is None else int(qi[req])
+                assert recs[k] == (rb, re, qb, mi[r])
+                assert ends[k] == mi[r + 1] and mi[r + 1] - mi[r] >= 2
+
+
 def _visible_pages(kv, qo, toks, P, causal, window):
     """Pages holding a key that some query token of ``toks`` sees, straight
     from the definition: token t (position p = kv - qo + t) sees key j iff
