@@ -377,9 +377,11 @@ int fi_version(void) { return 100; }
 
 int fi_default_workers(int kind, int num_cus, int num_kv_heads) {
   if (num_cus < 1 || num_kv_heads < 1) return 1;
-  // decode: 6 one-wave workgroups per CU (1.5 waves per SIMD: every worker
-  // resident, none waiting for a slot); prefill: 2 workgroups of 4 waves per CU
-  const int per_cu = kind == FI_KIND_PREFILL ? 2 : 6;
+  // decode: 5 one-wave workgroups per CU (every worker resident, none
+  // waiting for a slot; with the fixed cost a plan charges per decode item,
+  // 5 gave the llama8b_decode step 116.0 us against 118.2 at 6, and the
+  // skewed and mixed steps no slower); prefill: 2 workgroups of 4 waves per CU
+  const int per_cu = kind == FI_KIND_PREFILL ? 2 : 5;
   int w = per_cu * num_cus / num_kv_heads;
   return w < 1 ? 1 : w;
 }
