@@ -346,17 +346,26 @@ def prefill_page_size_measurements(ps, steps):
     """The prefill slice's 16 requests (same query and KV lengths) stored with
     pages of 1, 4, 16 and 64 tokens (pages of 1 token: the column-vector
     BSR of the pages), each batch drawn by the same generator, so only the
-    page size differs."""
+    page size differs.
+    The page sizes are timed in turn, five rounds (fresh device copies of the
+    pools each time, so their placement in memory varies), and each reports its
+    median round, so that a drift of the clock during the leg does not land
+    on one page size only."""
     import workloads as wl
     fl = prefill_flops(ps)
-    out = {"workload": "mixed_ragged_step prefill requests, page size 1 / 4 / 16 / 64", "flops": fl}
-    for P in (1, 4, 16, 64):
-        b = wl.make_batch(1009, ps.qo_lens, ps.kv_lens, page_size=P, num_qo_heads=ps.num_qo_heads,
-                          num_kv_heads=ps.num_kv_heads, head_dim=ps.head_dim, dtype=ps.dtype, causal=True,
-                          name=f"prefill_slice_P{P}")
-        ms, _ = time_batch_call(b, steps, 3)
+    out = {"workload": "mixed_ragged_step prefill requests, page size 1 / 4 / 16 / 64", "flops": fl,
+           "rounds": 5}
+    sizes = (1, 4, 16, 64)
+    batches = {P: wl.make_batch(1009, ps.qo_lens, ps.kv_lens, page_size=P, num_qo_heads=ps.num_qo_heads,
+                                num_kv_heads=ps.num_kv_heads, head_dim=ps.head_dim, dtype=ps.dtype,
+                                causal=True, name=f"prefill_slice_P{P}") for P in sizes}
+    times = {P: [] for P in sizes}
+    for _ in range(out["rounds"]):
+        for P in sizes:
+            times[P].append(time_batch_call(batches[P], steps, 3)[0])
+    for P in sizes:
+        ms = float(np.median(times[P]))
         out[f"P{P}"] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
-        del b
     out["P1_over_P16"] = round(out["P1"]["ms"] / out["P16"]["ms"], 3)
     return out
 
